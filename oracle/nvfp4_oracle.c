@@ -1,0 +1,298 @@
+/*
+ * nvfp4_oracle.c -- plain, slow fp64 CPU oracle for the NVFP4 weight x bf16
+ * activation matrix-vector path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or constant with the
+ * HIP library: every constant below is written out here from the format's
+ * definition.
+ *
+ * Sources.  The pages this method comes from name the format but never spell
+ * it out:
+ *   - bw24 wiki (GitHub), feature list, "NVFP4 (W4) decode path" item:
+ *     block-scaled FP4 weights read by a matvec for decode and by a wider
+ *     GEMM for prefill; the same list appears in the bw24 README (wpnews page
+ *     "Bw24 - from scratch rust+CUDA inference, every kernel tuned for
+ *     sm_120a").
+ *   - qwentin README (gitlite mirror), "Why it's interesting": its E2M1 4-bit
+ *     weight mode sits in the NVFP4 quality class, i.e. the NVFP4 element is
+ *     E2M1.
+ *   - bw24 README / wiki, "FP8 (e4m3)" KV option and the qwentin README's
+ *     "E4M3 V" cache: the FP8 flavour these engines use is E4M3.
+ * The format this oracle implements is therefore: E2M1 4-bit element codes,
+ * one E4M3 scale byte per 16 consecutive elements of a row, and one fp32
+ * tensor scale.  Every reading the pages leave open (OCP "FN" E4M3, nibble
+ * order, rounding, saturation, signed zero) is stated at the function that
+ * takes it.
+ *
+ * Arithmetic.  Every E2M1, E4M3, bf16 and fp32 value is a dyadic rational
+ * that fp64 holds exactly, and so is every product w_hat * x used here
+ * (E2M1: 2 significant bits, E4M3: 4, fp32 tensor scale: 24, bf16: 8 -- at
+ * most 38 bits).  Rounding happens only in the fp64 sums and where a
+ * function says so.
+ *
+ * Row-parallel loops use OpenMP over output rows only; each row's k-sum is a
+ * single sequential loop, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- decode -- */
+
+/* E2M1 code (4 bits) -> exact value.  Bit 3 sign, bits 2..1 exponent (bias 1),
+ * bit 0 mantissa; exponent field 0 is subnormal (0 or 0.5).  No inf, no NaN.
+ * Magnitudes of codes 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double oracle_e2m1_value(int code)
+{
+    int s = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double mag;
+    if (e == 0)
+        mag = 0.5 * m;
+    else
+        mag = (1.0 + 0.5 * m) * ldexp(1.0, e - 1);
+    return s ? -mag : mag;
+}
+
+/* E4M3 byte -> exact value, OCP "FN" variant: bit 7 sign, bits 6..3 exponent
+ * (bias 7), bits 2..0 mantissa; exponent 0 is subnormal (m/8 * 2^-6); the
+ * only NaNs are 0x7F and 0xFF; no infinities; largest finite 448 (0x7E). */
+double oracle_e4m3_value(int byte)
+{
+    int s = (byte >> 7) & 1;
+    int e = (byte >> 3) & 15;
+    int m = byte & 7;
+    double mag;
+    if ((byte & 0x7F) == 0x7F)
+        return NAN;
+    if (e == 0)
+        mag = (m / 8.0) * ldexp(1.0, -6);
+    else
+        mag = (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* bf16 bit pattern -> exact value (the fp32 whose upper half it is). */
+double oracle_bf16_value(uint16_t u)
+{
+    uint32_t bits = (uint32_t)u << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* ---------------------------------------------------------------- encode -- */
+
+/* Round a non-negative value q to the nearest E4M3 "FN" value, ties to the
+ * even mantissa code, saturating at 448 and never producing NaN; subnormals
+ * are kept.  Returns the byte (sign bit 0).
+ *
+ * Written as a search: walk the 127 finite non-negative codes in increasing
+ * value order and pick the nearest, a tie going to the even code.  The
+ * comparison uses midpoints between neighbours, which are exact in fp64. */
+uint8_t oracle_e4m3_encode(double q)
+{
+    int best = 0;
+    if (!(q > 0.0))
+        return 0;
+    if (q >= 448.0)
+        return 0x7E;
+    for (int c = 0; c < 0x7E; ++c) {
+        double lo = oracle_e4m3_value(c);
+        double hi = oracle_e4m3_value(c + 1);
+        double mid = 0.5 * (lo + hi);          /* exact: both dyadic, 5 bits */
+        if (q < mid) { best = c; break; }
+        if (q == mid) { best = (c % 2 == 0) ? c : c + 1; break; }
+        best = c + 1;
+    }
+    return (uint8_t)best;
+}
+
+/* Round a non-negative magnitude v to the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}
+ * with ties to the even code and saturation at 6.  Returns the 3-bit
+ * magnitude code.  Midpoints between neighbours (0.25, 0.75, 1.25, 1.75, 2.5,
+ * 3.5, 5) are exact in fp64. */
+int oracle_e2m1_encode_mag(double v)
+{
+    for (int c = 0; c < 7; ++c) {
+        double lo = oracle_e2m1_value(c);
+        double hi = oracle_e2m1_value(c + 1);
+        double mid = 0.5 * (lo + hi);
+        if (v < mid) return c;
+        if (v == mid) return (c % 2 == 0) ? c : c + 1;
+    }
+    return 7;
+}
+
+/* Quantise an fp32 matrix W[R][K] (row-major, K % 16 == 0) to NVFP4 in the
+ * canonical layout:
+ *   codes  [R][K/2]  byte k/2 of a row holds element k in its low nibble when
+ *                    k is even and in its high nibble when k is odd;
+ *   scales [R][K/16] one E4M3 byte per 16-element block, row-major.
+ * Per block b of a row:  s_b = E4M3_RNE(amax_b / (6 * tscale))  (saturating
+ * at 448), then  code_i = sign(w_i) | E2M1_RNE(|w_i| / (s_b * tscale)).
+ * A block whose scale rounds to 0 gets all-zero codes.  The sign bit of a
+ * code copies the sign bit of w (so a negative w rounding to 0 gives code 8).
+ *
+ * Decisions are taken on fp64 quotients.  fp64 is enough to make them
+ * exactly: a quotient of two values with at most 24+3 and 24+4 significant
+ * bits that is not exactly on a rounding midpoint lies at least 2^-32
+ * relatively away from it, far more than one fp64 rounding (2^-53). */
+void oracle_quantize(const float *W, int64_t R, int64_t K, float tscale,
+                     uint8_t *codes, uint8_t *scales)
+{
+    int64_t KB = K / 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t b = 0; b < KB; ++b) {
+            const float *w = W + r * K + b * 16;
+            double amax = 0.0;
+            for (int i = 0; i < 16; ++i) {
+                double a = fabs((double)w[i]);
+                if (a > amax) amax = a;
+            }
+            uint8_t sb = oracle_e4m3_encode(amax / (6.0 * (double)tscale));
+            scales[r * KB + b] = sb;
+            double denom = oracle_e4m3_value(sb) * (double)tscale;
+            for (int i = 0; i < 16; i += 2) {
+                int c[2];
+                for (int h = 0; h < 2; ++h) {
+                    if (sb == 0) { c[h] = 0; continue; }
+                    double v = fabs((double)w[i + h]) / denom;
+                    c[h] = oracle_e2m1_encode_mag(v) | (signbit(w[i + h]) ? 8 : 0);
+                }
+                codes[r * (K / 2) + b * 8 + i / 2] = (uint8_t)(c[0] | (c[1] << 4));
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------- dequant / gemv -- */
+
+/* Exact dequantised value of element (r, k): e2m1(code) * e4m3(scale) * tscale. */
+static double w_hat(const uint8_t *codes, const uint8_t *scales, float tscale,
+                    int64_t K, int64_t r, int64_t k)
+{
+    uint8_t byte = codes[r * (K / 2) + k / 2];
+    int code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+    return oracle_e2m1_value(code) * oracle_e4m3_value(scales[r * (K / 16) + k / 16])
+           * (double)tscale;
+}
+
+/* out[r][k] = exact w_hat (fp64 holds it exactly). */
+void oracle_dequant(const uint8_t *codes, const uint8_t *scales, float tscale,
+                    int64_t R, int64_t K, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k)
+            out[r * K + k] = w_hat(codes, scales, tscale, K, r, k);
+}
+
+/* Matrix-vector product for a list of output rows.
+ *   X    bf16 bit patterns [N][K] row-major (column n of the product is X[n]);
+ *   rows the nrows output rows to compute (each in [0, R));
+ *   Y    [N][nrows]:  Y[n][i] = sum_k w_hat[rows[i]][k] * x_n[k], fp64, k ascending;
+ *   S    [N][nrows]:  S[n][i] = sum_k |w_hat[rows[i]][k] * x_n[k]|  (the
+ *        magnitude sum that scales the parity tolerance); may be NULL. */
+void oracle_gemv_rows(const uint8_t *codes, const uint8_t *scales, float tscale,
+                      int64_t R, int64_t K, const uint16_t *X, int64_t N,
+                      const int64_t *rows, int64_t nrows, double *Y, double *S)
+{
+    (void)R;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t r = rows[i];
+        for (int64_t n = 0; n < N; ++n) {
+            double y = 0.0, s = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = w_hat(codes, scales, tscale, K, r, k)
+                           * oracle_bf16_value(X[n * K + k]);
+                y += p;
+                s += fabs(p);
+            }
+            Y[n * nrows + i] = y;
+            if (S) S[n * nrows + i] = s;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- swiglu -- */
+
+/* SiLU(gate) * up in fp64 for gate||up rows stacked as gu[N][2F] (gate in
+ * columns 0..F-1, up in F..2F-1):  h[n][i] = g * u / (1 + exp(-g)). */
+void oracle_swiglu(const float *gu, int64_t F, int64_t N, double *h)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t i = 0; i < F; ++i) {
+            double g = gu[n * 2 * F + i];
+            double u = gu[n * 2 * F + F + i];
+            h[n * F + i] = g * u / (1.0 + exp(-g));
+        }
+}
+
+/* fp64 -> bf16 bit pattern, round to nearest, ties to even (finite input,
+ * result within bf16 range).  Written on the value: find the bf16 grid
+ * spacing at v and round v / spacing with rint (fp64 default mode is
+ * round-to-nearest-even; the division by a power of two is exact). */
+uint16_t oracle_bf16_rne(double v)
+{
+    if (v == 0.0)
+        return signbit(v) ? 0x8000 : 0x0000;
+    double a = fabs(v);
+    int e;
+    frexp(a, &e);                       /* a = f * 2^e, f in [0.5, 1) */
+    int ulp_exp = e - 8;                /* bf16 has 8 significant bits */
+    if (ulp_exp < -133) ulp_exp = -133; /* subnormal spacing 2^-133 */
+    double q = rint(ldexp(a, -ulp_exp));
+    double r = ldexp(q, ulp_exp);
+    float f = (float)r;                 /* exact: r is a bf16 value */
+    uint32_t bits;
+    memcpy(&bits, &f, sizeof bits);
+    uint16_t out = (uint16_t)(bits >> 16);
+    return signbit(v) ? (uint16_t)(out | 0x8000) : out;
+}
+
+/* ---------------------------------------------------------------- repack -- */
+
+/* Reference of the library's repacked ("split-plane") layout, written from
+ * its published definition, not from the library's code.  The definition:
+ *   rows are grouped in tiles of 16; blocks (16 elements) of a row are
+ *   grouped in steps of 64; T = ceil(R/16), KB = K/16, S = ceil(KB/64);
+ *   code plane  [T][S][8][64][16 bytes]: entry (t, j, q, l) holds the 8
+ *     canonical code bytes of block b = 64j + l of row 16t + 2q in bytes
+ *     0..7 and the same block of row 16t + 2q + 1 in bytes 8..15;
+ *   scale plane [T][S][64][16 bytes]: entry (t, j, l) byte i is the scale
+ *     of block 64j + l of row 16t + i;
+ *   positions past the last row or block hold 0.
+ * The inverse is checked separately. */
+void oracle_repack(const uint8_t *codes, const uint8_t *scales, int64_t R, int64_t K,
+                   uint8_t *wq, uint8_t *ws)
+{
+    int64_t KB = K / 16;
+    int64_t T = (R + 15) / 16;
+    int64_t S = (KB + 63) / 64;
+    memset(wq, 0, (size_t)(T * S * 8 * 64 * 16));
+    memset(ws, 0, (size_t)(T * S * 64 * 16));
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < S; ++j)
+            for (int64_t l = 0; l < 64; ++l) {
+                int64_t b = 64 * j + l;
+                if (b >= KB) continue;
+                for (int64_t q = 0; q < 8; ++q)
+                    for (int64_t h = 0; h < 2; ++h) {
+                        int64_t r = 16 * t + 2 * q + h;
+                        if (r >= R) continue;
+                        uint8_t *dst = wq + (((t * S + j) * 8 + q) * 64 + l) * 16 + 8 * h;
+                        memcpy(dst, codes + r * (K / 2) + 8 * b, 8);
+                    }
+                for (int64_t i = 0; i < 16; ++i) {
+                    int64_t r = 16 * t + i;
+                    if (r >= R) continue;
+                    ws[((t * S + j) * 64 + l) * 16 + i] = scales[r * KB + b];
+                }
+            }
+}
