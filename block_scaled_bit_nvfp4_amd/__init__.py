@@ -1,0 +1,153 @@
+"""NVFP4 weight x bf16 activation matrix-vector products on MI355X (gfx950).
+
+A thin ctypes binding over ``libnvfp4.so``, whose C ABI is declared in
+``include/nvfp4.h``.  Every function below has the name of the C entry point
+it calls and only marshals arguments: torch tensors in device memory become
+raw pointers, and the current torch stream of the tensors' device becomes
+the HIP stream.  All arithmetic runs in the library's HIP kernels; if the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "NVFP4Error", "library_path", "load",
+    "nvfp4_strerror", "nvfp4_repacked_code_bytes", "nvfp4_repacked_scale_bytes",
+    "nvfp4_quantize", "nvfp4_repack", "nvfp4_dequant", "nvfp4_gemv",
+    "nvfp4_gemv_argmax_workspace_bytes", "nvfp4_gemv_argmax", "nvfp4_swiglu",
+    "alloc_repacked",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libnvfp4.so")
+_lock = threading.Lock()
+_lib = None
+
+NVFP4_MAX_N = 65536
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, nvfp4_strerror(status), status))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libnvfp4.so (built by ``python -m block_scaled_bit_nvfp4_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libnvfp4.so is not built (%s); run "
+                               "`python -m block_scaled_bit_nvfp4_amd.build`" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float,
+                                ctypes.c_size_t)
+        sigs = {
+            "nvfp4_strerror": (ctypes.c_char_p, [i32]),
+            "nvfp4_repacked_code_bytes": (sz, [i64, i64]),
+            "nvfp4_repacked_scale_bytes": (sz, [i64, i64]),
+            "nvfp4_quantize": (i32, [P, i64, i64, f32, P, P, P]),
+            "nvfp4_repack": (i32, [P, P, i64, i64, P, P, P]),
+            "nvfp4_dequant": (i32, [P, P, f32, i64, i64, P, P, P]),
+            "nvfp4_gemv": (i32, [P, P, f32, i64, i64, P, i32, P, P]),
+            "nvfp4_gemv_argmax_workspace_bytes": (sz, [i32]),
+            "nvfp4_gemv_argmax": (i32, [P, P, f32, i64, i64, P, i32, P, P, P, sz, P]),
+            "nvfp4_swiglu": (i32, [P, i64, i32, P, P]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor, got %r" % type(t))
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise NVFP4Error(status, where)
+
+
+def nvfp4_strerror(status: int) -> str:
+    return load().nvfp4_strerror(int(status)).decode()
+
+
+def nvfp4_repacked_code_bytes(rows: int, cols: int) -> int:
+    return int(load().nvfp4_repacked_code_bytes(rows, cols))
+
+
+def nvfp4_repacked_scale_bytes(rows: int, cols: int) -> int:
+    return int(load().nvfp4_repacked_scale_bytes(rows, cols))
+
+
+def nvfp4_gemv_argmax_workspace_bytes(n: int) -> int:
+    return int(load().nvfp4_gemv_argmax_workspace_bytes(n))
+
+
+def nvfp4_quantize(W, rows, cols, tscale, codes, scales, stream=None):
+    _check(load().nvfp4_quantize(_ptr(W), rows, cols, float(tscale), _ptr(codes), _ptr(scales),
+                                 _stream(stream, W)), "nvfp4_quantize")
+
+
+def nvfp4_repack(codes, scales, rows, cols, wq, ws, stream=None):
+    _check(load().nvfp4_repack(_ptr(codes), _ptr(scales), rows, cols, _ptr(wq), _ptr(ws),
+                               _stream(stream, codes)), "nvfp4_repack")
+
+
+def nvfp4_dequant(wq, ws, tscale, rows, cols, out_f32=None, out_bf16=None, stream=None):
+    _check(load().nvfp4_dequant(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(out_f32),
+                                _ptr(out_bf16), _stream(stream, wq)), "nvfp4_dequant")
+
+
+def nvfp4_gemv(wq, ws, tscale, rows, cols, X, n, Y, stream=None):
+    _check(load().nvfp4_gemv(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(X), int(n), _ptr(Y),
+                             _stream(stream, wq)), "nvfp4_gemv")
+
+
+def nvfp4_gemv_argmax(wq, ws, tscale, rows, cols, X, n, logits, argmax, workspace, stream=None):
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().nvfp4_gemv_argmax(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(X), int(n),
+                                    _ptr(logits), _ptr(argmax), _ptr(workspace), nbytes,
+                                    _stream(stream, wq)), "nvfp4_gemv_argmax")
+
+
+def nvfp4_swiglu(gu, F, n, h, stream=None):
+    _check(load().nvfp4_swiglu(_ptr(gu), int(F), int(n), _ptr(h), _stream(stream, gu)), "nvfp4_swiglu")
+
+
+def alloc_repacked(rows: int, cols: int, device="cuda"):
+    """Allocate (uninitialised) code and scale planes for nvfp4_repack."""
+    nq, ns = nvfp4_repacked_code_bytes(rows, cols), nvfp4_repacked_scale_bytes(rows, cols)
+    if nq == 0:
+        raise NVFP4Error(-2, "alloc_repacked")
+    return (torch.empty(nq, dtype=torch.uint8, device=device),
+            torch.empty(ns, dtype=torch.uint8, device=device))

@@ -1,0 +1,45 @@
+// nvfp4_host.h -- host-side argument checks and launch helpers shared by the
+// C-ABI entry points of libnvfp4.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nvfp4.h"
+#include "nvfp4_device.h"
+
+#define NVFP4_API extern "C" __attribute__((visibility("default")))
+
+namespace nvfp4 {
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// rows x cols must describe whole 16-element blocks and stay addressable with
+// 64-bit offsets and 32-bit tile/block counts.
+inline int check_shape(int64_t rows, int64_t cols) {
+    if (rows < 1 || cols < 16 || cols % 16 != 0) return NVFP4_ESHAPE;
+    if (rows > (int64_t(1) << 31) - 16 || cols > (int64_t(1) << 31) - 1024) return NVFP4_ESHAPE;
+    if (rows > (int64_t(1) << 62) / cols) return NVFP4_ESHAPE;
+    return NVFP4_OK;
+}
+
+inline bool tscale_ok(float t) { return t > 0.0f && t <= 3.4028234663852886e38f; }
+
+struct Geometry {
+    int64_t rows, cols;
+    int64_t kb;     // 16-element blocks per row
+    int64_t tiles;  // 16-row tiles
+    int64_t steps;  // steps of 64 blocks
+    Geometry(int64_t r, int64_t c)
+        : rows(r), cols(c), kb(c / kBlock), tiles(ceil_div(r, kTileRows)),
+          steps(ceil_div(c / kBlock, kLanes)) {}
+    size_t code_bytes() const { return size_t(tiles) * size_t(steps) * kRowPairs * kLanes * 16; }
+    size_t scale_bytes() const { return size_t(tiles) * size_t(steps) * kLanes * 16; }
+};
+
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,239 @@
+// nvfp4_quant.hip -- quantise, repack and dequantise kernels (gfx950) and
+// their C-ABI entry points.
+//
+// quantise: fp32 -> canonical NVFP4, the at-load re-encode of higher
+//   precision weights (bw24 wiki, feature list, safetensors-loader item).
+// repack:   canonical -> split-plane tiles read by the products (bw24 wiki,
+//   feature list, NVFP4 decode-path item; the loader's NVFP4 repack is
+//   byte-exact, and so is this one).
+// dequant:  repacked -> fp32 / bf16, a verification export of the decode.
+#include "nvfp4_host.h"
+
+namespace nvfp4 {
+
+// ----------------------------------------------------------------- quantise
+
+// Nearest E4M3 byte to q >= 0 (ties to even mantissa, saturating at 448,
+// subnormal spacing 2^-9).  q / quantum is an exact power-of-two scaling, and
+// rint() rounds half to even in the default rounding mode.
+__device__ __forceinline__ uint32_t e4m3_rne(double q) {
+    if (!(q > 0.0)) return 0u;
+    if (q >= 448.0) return 0x7Eu;
+    int e;
+    (void)frexp(q, &e);            // q in [2^(e-1), 2^e)
+    int E = e - 1;                  // unbiased exponent of q
+    if (E < -6) {                   // subnormal range: m * 2^-9, m in [0, 8]
+        double m = rint(ldexp(q, 9));
+        return uint32_t(m);         // m == 8 encodes 2^-6 (0x08), still right
+    }
+    double m = rint(ldexp(q, 3 - E));   // in [8, 16]
+    return uint32_t((E + 7) << 3) + uint32_t(m) - 8u;   // m == 16 carries into E
+}
+
+// E2M1 magnitude code of v >= 0, nearest with ties to the even code,
+// saturating at 6.  Midpoints 0.25 .. 5 are exact; at a midpoint whose upper
+// neighbour has the even code the comparison is >=, otherwise >.
+__device__ __forceinline__ uint32_t e2m1_rne_mag(double v) {
+    return uint32_t(v > 0.25) + uint32_t(v >= 0.75) + uint32_t(v > 1.25) + uint32_t(v >= 1.75) +
+           uint32_t(v > 2.5) + uint32_t(v >= 3.5) + uint32_t(v > 5.0);
+}
+
+// Exact value of an E4M3 byte as fp64 (finite bytes only: the quantiser
+// never produces 0x7F).
+__device__ __forceinline__ double e4m3_f64(uint32_t b) {
+    uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    return e == 0 ? ldexp(double(m), -9) : ldexp(double(8u + m), int(e) - 10);
+}
+
+// One thread per 16-element block.
+__global__ void __launch_bounds__(256) quantize_kernel(const float4 *__restrict__ W, int64_t nblocks,
+                                                       float tscale, uint2 *__restrict__ codes,
+                                                       uint8_t *__restrict__ scales) {
+    int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= nblocks) return;
+    float w[16];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        float4 f = W[i * 4 + v];
+        w[4 * v + 0] = f.x; w[4 * v + 1] = f.y; w[4 * v + 2] = f.z; w[4 * v + 3] = f.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(w[k]));
+    const double t = double(tscale);
+    uint32_t sb = e4m3_rne(double(amax) / (6.0 * t));
+    uint32_t out[2] = {0u, 0u};
+    if (sb != 0u) {
+        const double denom = e4m3_f64(sb) * t;     // exact: 4 x 24 significant bits
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            uint32_t c = e2m1_rne_mag(fabs(double(w[k])) / denom);
+            c |= signbit(w[k]) ? 8u : 0u;
+            out[k >> 3] |= c << (4 * (k & 7));
+        }
+    }
+    codes[i] = make_uint2(out[0], out[1]);
+    scales[i] = uint8_t(sb);
+}
+
+// ------------------------------------------------------------------- repack
+
+// Threads [0, code_units) write one 16-byte code entry each; threads
+// [code_units, code_units + scale_units) one 16-byte scale entry each.
+__global__ void __launch_bounds__(256) repack_kernel(const uint8_t *__restrict__ codes,
+                                                     const uint8_t *__restrict__ scales,
+                                                     int64_t rows, int64_t cols, int64_t steps,
+                                                     int64_t code_units, int64_t scale_units,
+                                                     uint4 *__restrict__ wq, uint4 *__restrict__ ws) {
+    int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t kb = cols / kBlock;
+    if (u < code_units) {
+        // u = ((t * steps + j) * 8 + q) * 64 + l
+        int64_t l = u % kLanes, rest = u / kLanes;
+        int64_t q = rest % kRowPairs;
+        rest /= kRowPairs;
+        int64_t j = rest % steps, t = rest / steps;
+        int64_t b = j * kLanes + l;
+        int64_t r0 = t * kTileRows + 2 * q;
+        uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+        if (b < kb) {
+            if (r0 < rows) lo = *reinterpret_cast<const uint2 *>(codes + r0 * (cols / 2) + b * 8);
+            if (r0 + 1 < rows) hi = *reinterpret_cast<const uint2 *>(codes + (r0 + 1) * (cols / 2) + b * 8);
+        }
+        wq[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        return;
+    }
+    u -= code_units;
+    if (u >= scale_units) return;
+    // u = (t * steps + j) * 64 + l
+    int64_t l = u % kLanes, rest = u / kLanes;
+    int64_t j = rest % steps, t = rest / steps;
+    int64_t b = j * kLanes + l;
+    uint32_t v[4] = {0u, 0u, 0u, 0u};
+    if (b < kb) {
+#pragma unroll
+        for (int i = 0; i < kTileRows; ++i) {
+            int64_t r = t * kTileRows + i;
+            if (r < rows) v[i >> 2] |= uint32_t(scales[r * kb + b]) << (8 * (i & 3));
+        }
+    }
+    ws[u] = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// ------------------------------------------------------------------ dequant
+
+// One thread per 16-byte code entry: 2 rows x 16 elements.
+__global__ void __launch_bounds__(256) dequant_kernel(const uint4 *__restrict__ wq,
+                                                      const uint4 *__restrict__ ws, float tscale,
+                                                      int64_t rows, int64_t cols, int64_t steps,
+                                                      int64_t code_units, float *__restrict__ out_f32,
+                                                      uint16_t *__restrict__ out_bf16) {
+    int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (u >= code_units) return;
+    int64_t l = u % kLanes, rest = u / kLanes;
+    int64_t q = rest % kRowPairs;
+    rest /= kRowPairs;
+    int64_t j = rest % steps, t = rest / steps;
+    const int64_t b = j * kLanes + l;
+    if (b >= cols / kBlock) return;
+    const uint4 c = wq[u];
+    const uint4 sc = ws[(t * steps + j) * kLanes + l];
+    const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t r = t * kTileRows + 2 * q + h;
+        if (r >= rows) break;
+        const int ri = 2 * int(q) + h;
+        const float s = e4m3_f32_dyn(sw[ri >> 2], ri & 3);
+        const uint32_t d[2] = {h ? c.z : c.x, h ? c.w : c.y};
+        uint32_t pairs[8];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            pairs[4 * w + 0] = as_u32(e2m1x2_bf16<0>(d[w]));
+            pairs[4 * w + 1] = as_u32(e2m1x2_bf16<1>(d[w]));
+            pairs[4 * w + 2] = as_u32(e2m1x2_bf16<2>(d[w]));
+            pairs[4 * w + 3] = as_u32(e2m1x2_bf16<3>(d[w]));
+        }
+        float v[16];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            v[2 * p + 0] = __uint_as_float(pairs[p] << 16) * s;          // exact
+            v[2 * p + 1] = __uint_as_float(pairs[p] & 0xFFFF0000u) * s;  // exact
+        }
+        const int64_t off = r * cols + b * kBlock;
+        if (out_bf16) {
+            uint4 *dst = reinterpret_cast<uint4 *>(out_bf16 + off);
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = (__float_as_uint(v[8 * p + 2 * e]) >> 16) |
+                           (__float_as_uint(v[8 * p + 2 * e + 1]) & 0xFFFF0000u);
+                dst[p] = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        if (out_f32) {
+            float4 *dst = reinterpret_cast<float4 *>(out_f32 + off);
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                dst[p] = make_float4(v[4 * p] * tscale, v[4 * p + 1] * tscale, v[4 * p + 2] * tscale,
+                                     v[4 * p + 3] * tscale);
+        }
+    }
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+NVFP4_API size_t nvfp4_repacked_code_bytes(int64_t rows, int64_t cols) {
+    return check_shape(rows, cols) == NVFP4_OK ? Geometry(rows, cols).code_bytes() : 0;
+}
+
+NVFP4_API size_t nvfp4_repacked_scale_bytes(int64_t rows, int64_t cols) {
+    return check_shape(rows, cols) == NVFP4_OK ? Geometry(rows, cols).scale_bytes() : 0;
+}
+
+NVFP4_API int nvfp4_quantize(const float *W, int64_t rows, int64_t cols, float tscale,
+                             uint8_t *codes, uint8_t *scales, hipStream_t stream) {
+    if (!W || !codes || !scales || !tscale_ok(tscale)) return NVFP4_EINVAL;
+    if (int st = check_shape(rows, cols)) return st;
+    if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 16)) return NVFP4_EALIGN;
+    const int64_t nblocks = rows * (cols / kBlock);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(ceil_div(nblocks, 256))), dim3(256), 0, stream,
+                       reinterpret_cast<const float4 *>(W), nblocks, tscale,
+                       reinterpret_cast<uint2 *>(codes), scales);
+    return launch_status();
+}
+
+NVFP4_API int nvfp4_repack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                           uint8_t *wq, uint8_t *ws, hipStream_t stream) {
+    if (!codes || !scales || !wq || !ws) return NVFP4_EINVAL;
+    if (int st = check_shape(rows, cols)) return st;
+    if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(wq, 16) || !aligned(ws, 16))
+        return NVFP4_EALIGN;
+    const Geometry g(rows, cols);
+    const int64_t code_units = int64_t(g.code_bytes() / 16), scale_units = int64_t(g.scale_bytes() / 16);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(repack_kernel, dim3(unsigned(ceil_div(code_units + scale_units, 256))), dim3(256),
+                       0, stream, codes, scales, rows, cols, g.steps, code_units, scale_units,
+                       reinterpret_cast<uint4 *>(wq), reinterpret_cast<uint4 *>(ws));
+    return launch_status();
+}
+
+NVFP4_API int nvfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
+                            int64_t cols, float *out_f32, uint16_t *out_bf16, hipStream_t stream) {
+    if (!wq || !ws || (!out_f32 && !out_bf16) || !tscale_ok(tscale)) return NVFP4_EINVAL;
+    if (int st = check_shape(rows, cols)) return st;
+    if (!aligned(wq, 16) || !aligned(ws, 16) || !aligned(out_f32, 16) || !aligned(out_bf16, 16))
+        return NVFP4_EALIGN;
+    const Geometry g(rows, cols);
+    const int64_t code_units = int64_t(g.code_bytes() / 16);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(dequant_kernel, dim3(unsigned(ceil_div(code_units, 256))), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4 *>(wq), reinterpret_cast<const uint4 *>(ws), tscale,
+                       rows, cols, g.steps, code_units, out_f32, out_bf16);
+    return launch_status();
+}

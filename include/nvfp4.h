@@ -1,0 +1,159 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4: NVFP4 weight x bf16 activation matrix-vector
+ * products on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages this library follows):
+ *   - bw24 wiki (GitHub) and bw24 README (wpnews page "Bw24 - from scratch
+ *     rust+CUDA inference, every kernel tuned for sm_120a"), feature list,
+ *     NVFP4 decode-path item: decode multiplies block-scaled FP4 weights by
+ *     the activation vector in a matvec fed by a "split-plane" repack of the
+ *     weights, a wider GEMM serves prefill, and the kernel is picked per
+ *     matrix shape; the MTP item: the K+1 draft tokens of a speculative round
+ *     are verified in one batched forward, so every weight is read once for
+ *     all K+1 columns.
+ *   - bw24 wiki, correctness gates and the exactness note after them: the
+ *     order of floating-point summation is part of the contract, and a
+ *     prefill-argmax vs decode-argmax gate precedes any timing.
+ *   - qwentin README (gitlite mirror), "Why it's interesting": NVFP4's
+ *     element is E2M1; "How it works": the speculative verify reads each
+ *     weight once for the whole tree, wide prefill reads it once for N
+ *     tokens, and the draft tree descends by a dense argmax.
+ *
+ * Format.  NVFP4 = E2M1 element codes (bias 1, values 0, .5, 1, 1.5, 2, 3, 4,
+ * 6 and their negatives), one E4M3 scale byte per 16 consecutive elements of
+ * a row (OCP "FN": bias 7, subnormals, max 448, NaN only at 0x7F/0xFF), and
+ * one fp32 tensor scale:  w_hat[r][k] = e2m1(code) * e4m3(scale) * tscale.
+ *
+ * Canonical layout (input of nvfp4_repack, output of nvfp4_quantize):
+ *   codes  uint8 [rows][cols/2]:  element k of a row sits in byte k/2, in the
+ *                                 low nibble when k is even, high when odd;
+ *   scales uint8 [rows][cols/16]: scale of elements 16b..16b+15 at [r][b].
+ *
+ * Repacked layout (what the products read; "split-plane": codes and scales
+ * are two separate planes).  Let T = ceil(rows/16) row tiles, KB = cols/16
+ * blocks per row, S = ceil(KB/64) steps of 64 blocks.
+ *   code plane  uint8 [T][S][8][64][16]: entry (t, j, q, l) holds the 8
+ *       canonical code bytes of block b = 64j + l of row 16t + 2q in bytes
+ *       0..7 and of row 16t + 2q + 1 in bytes 8..15;
+ *   scale plane uint8 [T][S][64][16]: byte i of entry (t, j, l) is the scale
+ *       of block 64j + l of row 16t + i;
+ *   positions past the last row or block hold 0.
+ * One 64-lane wavefront reads one (t, j, q) code entry as 64 x 16 contiguous
+ * bytes and one (t, j) scale entry likewise: 128-bit coalesced loads, each
+ * byte once per call for all N columns.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are device memory owned by the caller; the library
+ *     allocates nothing and keeps no state between calls.  Inputs must not be
+ *     modified, and outputs not read, until the call's work on `stream` is
+ *     done.  `stream` may be NULL (the null stream).
+ *   - Calls are asynchronous and stream-ordered: arguments are validated on
+ *     the host, kernels are enqueued on `stream`, and the call returns
+ *     without waiting.  No host synchronisation, no device allocation.
+ *   - Pointers to weights, activations and fp32 matrices must be 16-byte
+ *     aligned (NVFP4_EALIGN otherwise); row lengths follow from cols % 16.
+ *   - Activations X are bf16 bit patterns [n][cols] row-major; outputs Y are
+ *     fp32 [n][rows] row-major (column c of the product is X[c], Y[c]).
+ *   - Return value: NVFP4_OK or a negative NVFP4_E* code; nvfp4_strerror
+ *     names it.  On an error nothing has been enqueued, except for
+ *     NVFP4_EHIP (a launch failed; earlier launches of the call may have run).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_OK 0
+#define NVFP4_EINVAL (-1)     /* null pointer, n out of range, tscale not finite and > 0 */
+#define NVFP4_ESHAPE (-2)     /* rows < 1, cols < 16, cols % 16 != 0, or a size overflows */
+#define NVFP4_EALIGN (-3)     /* a pointer is not 16-byte aligned (2-/4-byte for outputs) */
+#define NVFP4_EWORKSPACE (-4) /* workspace smaller than nvfp4_gemv_argmax_workspace_bytes */
+#define NVFP4_EHIP (-5)       /* a kernel launch failed (e.g. no gfx950 device) */
+
+/* Largest n accepted by the products (columns of X). */
+#define NVFP4_MAX_N 65536
+
+/* Human-readable name of a status code; a static string, never NULL. */
+const char *nvfp4_strerror(int status);
+
+/* Sizes in bytes of the repacked code and scale planes for a rows x cols
+ * matrix (rows padded to 16, blocks to 64), or 0 for an invalid shape. */
+size_t nvfp4_repacked_code_bytes(int64_t rows, int64_t cols);
+size_t nvfp4_repacked_scale_bytes(int64_t rows, int64_t cols);
+
+/* Quantise fp32 W [rows][cols] (finite values) to canonical NVFP4.
+ * Per 16-element block: scale = E4M3 nearest-even of amax / (6 * tscale),
+ * saturating at 448; each code = sign bit of w | E2M1 nearest-even of
+ * |w| / (scale * tscale), saturating at 6; a block whose scale is 0 gets all
+ * zero codes.  The rounding decisions are exact (taken on fp64 quotients).
+ * The pages re-encode higher-precision checkpoints to NVFP4 at load (bw24
+ * wiki, feature list, safetensors-loader item); the rule above is the
+ * common amax/6 block scaling.  codes [rows][cols/2], scales [rows][cols/16]. */
+int nvfp4_quantize(const float *W, int64_t rows, int64_t cols, float tscale,
+                   uint8_t *codes, uint8_t *scales, hipStream_t stream);
+
+/* Canonical (codes, scales) -> repacked (wq, ws), a pure byte permutation
+ * plus zero padding (bw24 wiki, feature list: "split-plane repack" of the
+ * NVFP4 decode path; its safetensors loader repacks NVFP4 byte-exactly).
+ * wq holds nvfp4_repacked_code_bytes(rows, cols) bytes, ws
+ * nvfp4_repacked_scale_bytes(rows, cols); every byte of both is written. */
+int nvfp4_repack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                 uint8_t *wq, uint8_t *ws, hipStream_t stream);
+
+/* Dequantise a repacked matrix to canonical row-major outputs (either may be
+ * NULL, not both):
+ *   out_f32  [rows][cols] fp32: e2m1 * e4m3 * tscale rounded once to fp32;
+ *   out_bf16 [rows][cols] bf16 bits: e2m1 * e4m3 (tensor scale excluded),
+ *            exact because the product has at most 6 significant bits.
+ * NaN scale bytes give NaN.  A verification export of the decode the
+ * products use. */
+int nvfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
+                  float *out_f32, uint16_t *out_bf16, hipStream_t stream);
+
+/* Y[c][r] = tscale * sum_k e2m1(code[r][k]) * e4m3(scale[r][k/16]) * X[c][k]
+ * for c < n, r < rows (bw24 wiki, feature list: the NVFP4 decode matvec and
+ * the batched K+1 verify; qwentin README, "How it works": each weight read
+ * once for all columns; wide prefill for large n).
+ * Products are exact in fp32 and accumulate in fp32 in a fixed order that
+ * depends only on (rows, cols): results are bitwise reproducible run to run,
+ * and for n <= 8 column c equals, bit for bit, the n = 1 product of X[c]
+ * (bw24 wiki, exactness note: summation order is part of the contract).
+ * n <= 8 runs the VALU matvec; larger n runs a dequant-to-bf16 MFMA tile
+ * contraction.  1 <= n <= NVFP4_MAX_N.  X [n][cols] bf16 bits, Y [n][rows]. */
+int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
+               const uint16_t *X, int n, float *Y, hipStream_t stream);
+
+/* Workspace bytes nvfp4_gemv_argmax needs for n columns (8 * n), 0 if n is
+ * out of range. */
+size_t nvfp4_gemv_argmax_workspace_bytes(int n);
+
+/* nvfp4_gemv for 1 <= n <= 8 plus, per column c, argmax[c] = the lowest row
+ * index of the largest Y[c][r] (-0 and +0 compare equal) -- the vocabulary
+ * projection with the greedy token (bw24 wiki: prefill-argmax vs
+ * decode-argmax gate; qwentin README, "How it works": dense-argmax descent).
+ * logits [n][rows] may be NULL (not stored).  workspace: device memory of at
+ * least nvfp4_gemv_argmax_workspace_bytes(n) bytes, 8-byte aligned, which the
+ * call initialises itself; it must not be shared by calls in flight. */
+int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
+                      int64_t cols, const uint16_t *X, int n, float *logits, int32_t *argmax,
+                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* SwiGLU between the MLP matvecs: gu fp32 [n][2F] holds the stacked gate
+ * (columns 0..F-1) and up (F..2F-1) outputs; h [n][F] bf16 bits =
+ * bf16_nearest_even(g * u / (1 + exp(-g))) computed in fp32 (the pages'
+ * persistent-MLP decode GEMV, qwentin README "How it works", runs this
+ * step between its gate/up and down products).  1 <= n <= NVFP4_MAX_N,
+ * F >= 1; gu 16-byte aligned, h 4-byte aligned. */
+int nvfp4_swiglu(const float *gu, int64_t F, int n, uint16_t *h, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

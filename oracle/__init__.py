@@ -59,6 +59,8 @@ def _load():
         lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.c_void_p
         i64 = ctypes.c_int64
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
         lib.oracle_e2m1_value.restype = ctypes.c_double
         lib.oracle_e2m1_value.argtypes = [ctypes.c_int]
         lib.oracle_e4m3_value.restype = ctypes.c_double
@@ -97,6 +99,11 @@ def _check_shape(R: int, K: int):
 
 
 # ------------------------------------------------------------------ scalars --
+
+def num_threads() -> int:
+    """Threads the oracle's row-parallel loops use (OpenMP)."""
+    return int(_load().oracle_num_threads())
+
 
 def e2m1_value(code: int) -> float:
     return _load().oracle_e2m1_value(int(code))

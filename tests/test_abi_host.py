@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/nvfp4.h declares, computes plane sizes, and rejects
+bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_bit_nvfp4_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nv.library_path()):
+        from block_scaled_bit_nvfp4_amd import build
+        build.build(verbose=False)
+    return nv.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("nvfp4_repack", "nvfp4_gemv", "nvfp4_gemv_argmax", "nvfp4_quantize",
+                 "nvfp4_dequant", "nvfp4_swiglu", "nvfp4_strerror"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # and nothing from the internal namespace leaks as a C symbol
+    with pytest.raises(AttributeError):
+        getattr(lib, "launch_valu")
+
+
+def test_binding_names_match_header():
+    for name in declared_functions():
+        assert callable(getattr(nv, name)), name
+
+
+@pytest.mark.parametrize("rows,cols,code,scale", [
+    (256, 512, 16 * 1 * 8192, 16 * 1 * 1024),
+    (4096, 4096, 256 * 4 * 8192, 256 * 4 * 1024),
+    (17, 32, 2 * 8192, 2 * 1024),
+    (151936, 5120, 9496 * 5 * 8192, 9496 * 5 * 1024),
+    (5120, 17408, 320 * 17 * 8192, 320 * 17 * 1024),
+])
+def test_plane_sizes(lib, rows, cols, code, scale):
+    assert nv.nvfp4_repacked_code_bytes(rows, cols) == code
+    assert nv.nvfp4_repacked_scale_bytes(rows, cols) == scale
+
+
+@pytest.mark.parametrize("rows,cols", [(0, 512), (16, 0), (16, 8), (16, 24), (-1, 16), (16, 1 << 40)])
+def test_plane_sizes_invalid(lib, rows, cols):
+    assert nv.nvfp4_repacked_code_bytes(rows, cols) == 0
+    assert nv.nvfp4_repacked_scale_bytes(rows, cols) == 0
+
+
+def test_workspace_bytes(lib):
+    assert [nv.nvfp4_gemv_argmax_workspace_bytes(n) for n in (0, 1, 4, 8, 9)] == [0, 8, 32, 64, 0]
+
+
+def test_strerror(lib):
+    for code in (OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP):
+        assert nv.nvfp4_strerror(code)
+    assert nv.nvfp4_strerror(OK) == "ok"
+    assert nv.nvfp4_strerror(12345) == "unknown status"
+
+
+# Fake device addresses: validation rejects these calls before any HIP call,
+# so nothing is ever dereferenced or launched.
+A = ctypes.c_void_p(0x100000)       # 16-byte aligned
+B = ctypes.c_void_p(0x200000)
+C = ctypes.c_void_p(0x300000)
+MIS = ctypes.c_void_p(0x100008)     # 8-byte aligned only
+NULL = None
+S0 = None
+
+
+def test_gemv_validation(lib):
+    g = lib.nvfp4_gemv
+    assert g(NULL, B, 1.0, 16, 32, C, 1, A, S0) == EINVAL
+    assert g(A, B, 1.0, 16, 32, C, 0, A, S0) == EINVAL          # n = 0
+    assert g(A, B, 1.0, 16, 32, C, 65537, A, S0) == EINVAL      # n too large
+    assert g(A, B, 0.0, 16, 32, C, 1, A, S0) == EINVAL          # tscale <= 0
+    assert g(A, B, float("nan"), 16, 32, C, 1, A, S0) == EINVAL
+    assert g(A, B, float("inf"), 16, 32, C, 1, A, S0) == EINVAL
+    assert g(A, B, 1.0, 0, 32, C, 1, A, S0) == ESHAPE
+    assert g(A, B, 1.0, 16, 40, C, 1, A, S0) == ESHAPE
+    assert g(MIS, B, 1.0, 16, 32, C, 1, A, S0) == EALIGN
+    assert g(A, B, 1.0, 16, 32, MIS, 1, A, S0) == EALIGN
+    assert g(A, B, 1.0, 16, 32, C, 1, ctypes.c_void_p(0x100002), S0) == EALIGN
+    assert g(A, B, 1.0, 16, 32, C, 1, NULL, S0) == EINVAL
+
+
+def test_argmax_validation(lib):
+    g = lib.nvfp4_gemv_argmax
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, B, 31, S0) == EWORKSPACE
+    assert g(A, B, 1.0, 16, 32, C, 9, NULL, A, B, 1024, S0) == EINVAL   # argmax is n <= 8
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, NULL, B, 32, S0) == EINVAL
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, NULL, 32, S0) == EINVAL
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, ctypes.c_void_p(0x200004), 32, S0) == EALIGN
+
+
+def test_other_entry_points_validation(lib):
+    assert lib.nvfp4_quantize(A, 16, 32, 1.0, B, NULL, S0) == EINVAL
+    assert lib.nvfp4_quantize(A, 16, 33, 1.0, B, C, S0) == ESHAPE
+    assert lib.nvfp4_quantize(A, 16, 32, -1.0, B, C, S0) == EINVAL
+    assert lib.nvfp4_quantize(MIS, 16, 32, 1.0, B, C, S0) == EALIGN
+    assert lib.nvfp4_repack(A, B, 16, 32, C, NULL, S0) == EINVAL
+    assert lib.nvfp4_repack(A, B, 16, 32, C, MIS, S0) == EALIGN
+    assert lib.nvfp4_repack(A, B, 16, 0, C, A, S0) == ESHAPE
+    assert lib.nvfp4_dequant(A, B, 1.0, 16, 32, NULL, NULL, S0) == EINVAL
+    assert lib.nvfp4_dequant(A, B, 1.0, 16, 32, MIS, NULL, S0) == EALIGN
+    assert lib.nvfp4_swiglu(A, 0, 1, B, S0) == ESHAPE
+    assert lib.nvfp4_swiglu(A, 16, 0, B, S0) == EINVAL
+    assert lib.nvfp4_swiglu(MIS, 16, 1, B, S0) == EALIGN

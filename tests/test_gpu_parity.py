@@ -1,0 +1,279 @@
+"""GPU parity of the HIP library against the fp64 CPU oracle at sizes the
+oracle finishes in seconds (several tiles and steps, ragged tails), through
+the C ABI.  Bit-exact: quantise, repack, dequant, argmax.  Tolerance
+|y - y_ref| <= 1e-5 * sum|w*x| + 1e-6: the products."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import _gpu as G
+from tests.conftest import golden_lines
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_scaled_bit_nvfp4_amd as nv
+    nv.load()                       # fails loudly if the HIP library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ decode, exact
+
+def _all_codes_all_scales():
+    """256 rows x 512 cols: row r uses scale byte r in every block and holds
+    every code byte 0..255 once, so every (code, scale) pair appears."""
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    scales = np.tile(np.arange(256, dtype=np.uint8)[:, None], (1, 32))
+    return codes, scales
+
+
+@pytest.mark.parametrize("tscale", [1.0, 0.37, 2.0**-20, 1000.0])
+def test_dequant_exhaustive_code_scale_table(tscale):
+    codes, scales = _all_codes_all_scales()
+    R, K = 256, 512
+    G.note("dequant exhaustive tscale=%g" % tscale)
+    cd, sd = G.canonical_to_dev(codes, scales)
+    wq, ws = G.repack_gpu(cd, sd, R, K)
+    f32 = torch.empty(R, K, dtype=torch.float32, device=G.DEV)
+    b16 = torch.empty(R, K, dtype=torch.int16, device=G.DEV)
+    import block_scaled_bit_nvfp4_amd as nv
+    nv.nvfp4_dequant(wq, ws, tscale, R, K, f32, b16)
+    got32 = f32.cpu().numpy()
+    got16 = b16.cpu().numpy().view(np.uint16)
+    want32 = oracle.dequant_f32(codes, scales, tscale)
+    want16 = oracle.dequant_bf16_bits(codes, scales)
+    nan = np.isnan(want32)
+    assert nan.sum() == 2 * 512
+    assert np.array_equal(np.isnan(got32), nan)
+    assert np.array_equal(got32[~nan].view(np.uint32), want32[~nan].view(np.uint32))
+    g16 = (got16.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(np.isnan(g16), nan)
+    assert np.array_equal(got16[~nan], want16[~nan])
+
+
+# ---------------------------------------------------------- quantise, exact
+
+def test_quantize_hand_worked_blocks():
+    for line in golden_lines("quantize_blocks.txt"):
+        ts, ws_, sb, cb = [p.strip() for p in line.split("|")]
+        W = torch.tensor([[float(x) for x in ws_.split()]], dtype=torch.float32, device=G.DEV)
+        G.note("quantize golden block tscale=%s" % ts)
+        codes, scales = G.quantize_gpu(W, float(ts))
+        assert scales.cpu().numpy()[0, 0] == int(sb, 16), line
+        assert list(codes.cpu().numpy()[0]) == [int(x, 16) for x in cb.split()], line
+
+
+@pytest.mark.parametrize("R,K,seed,outliers,tscale", [
+    (256, 512, 0, False, 1.0),
+    (33, 1040, 1, True, 1.0),
+    (100, 2048, 2, True, 0.01),
+    (7, 16, 3, True, 3.0),
+])
+def test_quantize_bitexact(R, K, seed, outliers, tscale):
+    W = G.seeded_matrix(R, K, seed, outliers)
+    W[0, :16] *= 1e5                      # a saturated-scale block
+    W[-1, 16 % K:32 if K >= 32 else 16] = 0.0
+    G.note("quantize %dx%d seed %d" % (R, K, seed))
+    codes, scales = G.quantize_gpu(W, tscale)
+    c_ref, s_ref = oracle.quantize(W.cpu().numpy(), tscale)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+
+
+def test_quantize_exact_ties_and_signed_zero():
+    ties = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+    g = torch.Generator().manual_seed(4)
+    W = ties[torch.randint(0, 8, (16, 256), generator=g)] * (torch.randint(0, 2, (16, 256), generator=g) * 2 - 1)
+    W[:, ::16] = 6.0
+    W = W * 2.0**-5
+    W[3, 5] = -0.0
+    W = W.to(torch.float32).to(G.DEV)
+    G.note("quantize ties")
+    codes, scales = G.quantize_gpu(W)
+    c_ref, s_ref = oracle.quantize(W.cpu().numpy())
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+
+
+# ------------------------------------------------------------ repack, exact
+
+@pytest.mark.parametrize("R,K", [(17, 32), (16, 1024), (33, 1040), (1, 16), (50, 2064), (256, 512)])
+def test_repack_bytes_equal_reference(R, K):
+    rng = np.random.default_rng(R * 7 + K)
+    codes = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (R, K // 16), dtype=np.uint8)
+    G.note("repack %dx%d" % (R, K))
+    cd, sd = G.canonical_to_dev(codes, scales)
+    wq, ws = G.repack_gpu(cd, sd, R, K)
+    rq, rs = oracle.repack(codes, scales)
+    assert np.array_equal(wq.cpu().numpy(), rq)
+    assert np.array_equal(ws.cpu().numpy(), rs)
+
+
+# --------------------------------------------------------- products, tolerance
+
+def _prepare(R, K, seed, outliers=True, tscale=1.0):
+    W = G.seeded_matrix(R, K, seed, outliers)
+    codes, scales = G.quantize_gpu(W, tscale)
+    wq, ws = G.repack_gpu(codes, scales, R, K)
+    c_ref, s_ref = oracle.quantize(W.cpu().numpy(), tscale)
+    return wq, ws, c_ref, s_ref
+
+
+@pytest.mark.parametrize("R,K,n,tscale", [
+    (256, 512, 1, 1.0),        # the 256 x 512 single matvec, seed 0 weights
+    (100, 2064, 1, 1.0),       # ragged rows, a partial last step
+    (48, 3072, 2, 0.5),
+    (129, 4096, 3, 1.0),
+    (64, 5120, 4, 1.0),
+    (40, 1024, 5, 2.0),
+    (23, 1088, 6, 1.0),
+    (31, 96, 7, 1.0),
+    (300, 17408, 8, 1.0),
+    (16, 16, 1, 1.0),          # a single block
+])
+def test_gemv_parity(R, K, n, tscale):
+    seed = 0 if (R, K) == (256, 512) else R + K
+    wq, ws, c_ref, s_ref = _prepare(R, K, seed, outliers=(R, K) != (256, 512), tscale=tscale)
+    X = G.seeded_x(n, K, seed=seed + 1)
+    G.note("gemv %dx%d n=%d" % (R, K, n))
+    Y = G.gemv_gpu(wq, ws, tscale, R, K, X).cpu().numpy()
+    Y_ref, S = oracle.gemv(c_ref, s_ref, tscale, G.wl.bf16_bits(X))
+    G.assert_within_tolerance(Y, Y_ref, S, "gemv %dx%d n=%d" % (R, K, n))
+
+
+@pytest.mark.parametrize("n", [12, 33])
+def test_gemv_wide_parity(n):
+    R, K = 80, 1024
+    wq, ws, c_ref, s_ref = _prepare(R, K, 77)
+    X = G.seeded_x(n, K, seed=78)
+    G.note("gemv wide n=%d" % n)
+    Y = G.gemv_gpu(wq, ws, 1.0, R, K, X).cpu().numpy()
+    Y_ref, S = oracle.gemv(c_ref, s_ref, 1.0, G.wl.bf16_bits(X))
+    G.assert_within_tolerance(Y, Y_ref, S, "gemv wide n=%d" % n)
+
+
+def test_gemv_exact_special_cases():
+    R, K = 64, 2048
+    wq, ws, c_ref, s_ref = _prepare(R, K, 5)
+    w_hat32 = oracle.dequant_f32(c_ref, s_ref, 1.0)
+    # one-hot x: y[r] is w_hat[r][k] rounded to fp32, bit for bit (a sum whose
+    # other terms are +0 turns a -0 term into +0, so zeros compare as +0)
+    w_hat32 = w_hat32 + np.float32(0.0)
+    for k in (0, 1, 17, 1000, 2047):
+        x = torch.zeros(1, K, dtype=torch.bfloat16, device=G.DEV)
+        x[0, k] = 1.0
+        G.note("gemv one-hot k=%d" % k)
+        y = G.gemv_gpu(wq, ws, 1.0, R, K, x).cpu().numpy()[0]
+        assert np.array_equal(y.view(np.uint32), w_hat32[:, k].view(np.uint32)), k
+    X = G.seeded_x(1, K, seed=6)
+    y = G.gemv_gpu(wq, ws, 1.0, R, K, X)
+    # x = 0 -> 0; x -> -x flips every bit of sign only; tscale * 2^j scales exactly
+    z = G.gemv_gpu(wq, ws, 1.0, R, K, torch.zeros_like(X))
+    assert torch.count_nonzero(z).item() == 0
+    yn = G.gemv_gpu(wq, ws, 1.0, R, K, -X)
+    assert torch.equal(yn, -y)
+    for j in (-3, 5):
+        yj = G.gemv_gpu(wq, ws, 2.0**j, R, K, X)
+        assert torch.equal(yj, y * 2.0**j)
+
+
+def test_gemv_deterministic_and_column_identity():
+    R, K = 1040, 5120
+    wq, ws, _, _ = _prepare(R, K, 9)
+    X = G.seeded_x(8, K, seed=10)
+    G.note("gemv determinism")
+    ys = {}
+    for n in (1, 2, 4, 8):
+        ys[n] = G.gemv_gpu(wq, ws, 1.0, R, K, X[:n].contiguous())
+        again = G.gemv_gpu(wq, ws, 1.0, R, K, X[:n].contiguous())
+        assert torch.equal(ys[n].view(torch.int32), again.view(torch.int32)), n
+    for c in range(8):
+        single = G.gemv_gpu(wq, ws, 1.0, R, K, X[c:c + 1].contiguous())
+        for n in (2, 4, 8):
+            if c < n:
+                assert torch.equal(ys[n][c].view(torch.int32), single[0].view(torch.int32)), (c, n)
+
+
+# -------------------------------------------------------------- argmax, exact
+
+@pytest.mark.parametrize("n", [1, 4, 8])
+def test_argmax_matches_oracle(n):
+    R, K = 2000, 1024
+    wq, ws, c_ref, s_ref = _prepare(R, K, 11 + n)
+    X = G.seeded_x(n, K, seed=12)
+    G.note("argmax n=%d" % n)
+    logits, am = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, X)
+    Y_ref, S = oracle.gemv(c_ref, s_ref, 1.0, G.wl.bf16_bits(X))
+    G.assert_within_tolerance(logits.cpu().numpy(), Y_ref, S, "argmax logits")
+    assert list(am.cpu().numpy()) == list(oracle.argmax_first(Y_ref))
+    # logits are the same bits as the plain product
+    y = G.gemv_gpu(wq, ws, 1.0, R, K, X)
+    assert torch.equal(y.view(torch.int32), logits.view(torch.int32))
+    _, am2 = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, X, with_logits=False)
+    assert torch.equal(am, am2)
+
+
+def test_argmax_ties_take_lowest_index():
+    R, K = 300, 512
+    rng = np.random.default_rng(13)
+    codes = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales = rng.integers(0x20, 0x40, (R, K // 16), dtype=np.uint8)
+    # plant a row of large positive weights and copy it to later rows
+    codes[123] = 0x77
+    scales[123] = 0x48
+    for r in (5 + 123, 200, 299):
+        codes[r], scales[r] = codes[123], scales[123]
+    x = torch.ones(2, K, dtype=torch.bfloat16, device=G.DEV)
+    cd, sd = G.canonical_to_dev(codes, scales)
+    wq, ws = G.repack_gpu(cd, sd, R, K)
+    G.note("argmax ties")
+    logits, am = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, x)
+    assert list(am.cpu().numpy()) == [123, 123]
+    Y_ref, _ = oracle.gemv(codes, scales, 1.0, G.wl.bf16_bits(x))
+    assert list(oracle.argmax_first(Y_ref)) == [123, 123]
+    # all-zero logits: every row ties at 0 (with -0 = +0) -> row 0
+    z = torch.zeros(1, K, dtype=torch.bfloat16, device=G.DEV)
+    z[0, 0] = -0.0
+    _, am0 = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, z)
+    assert am0.item() == 0
+
+
+# -------------------------------------------------------------------- SwiGLU
+
+def _check_swiglu(gu: np.ndarray, h_bits: np.ndarray):
+    """h must be the nearest-even bf16 of the fp64 SwiGLU; where that value is
+    within 1e-6 (relative) of a bf16 rounding midpoint, either neighbour."""
+    h64 = oracle.swiglu(gu)
+    want = oracle.bf16_rne_array(h64)
+    diff = np.nonzero(h_bits != want)[0] if h_bits.ndim == 1 else np.argwhere(h_bits != want)
+    for idx in diff:
+        idx = tuple(np.atleast_1d(idx))
+        v = h64[idx]
+        got = float((np.array([h_bits[idx]], np.uint32) << 16).view(np.float32)[0])
+        lo_hi = sorted([got, float((np.array([want[idx]], np.uint32) << 16).view(np.float32)[0])])
+        mid = 0.5 * (lo_hi[0] + lo_hi[1])
+        assert abs(v - mid) <= 1e-6 * abs(v), (idx, v, got)
+
+
+@pytest.mark.parametrize("F,n", [(17408, 1), (1000, 4), (3, 2)])
+def test_swiglu_parity(F, n):
+    g = torch.Generator(device=G.DEV).manual_seed(F + n)
+    gu = (torch.randn(n, 2 * F, generator=g, device=G.DEV) * 3).to(torch.float32)
+    gu[0, 0] = 0.0
+    if F > 2:
+        gu[0, 1] = 80.0
+        gu[0, 2] = -80.0
+    h = torch.empty(n, F, dtype=torch.int16, device=G.DEV)
+    import block_scaled_bit_nvfp4_amd as nv
+    G.note("swiglu F=%d n=%d" % (F, n))
+    nv.nvfp4_swiglu(gu, F, n, h)
+    _check_swiglu(gu.cpu().numpy(), h.cpu().numpy().view(np.uint16))
