@@ -23,6 +23,9 @@ ARCH = "gfx950"
 CFLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-ffp-contract=off",                       # every fused multiply-add is written out
+    # dot2 as the three-operand VOP3P form: a chain can start from the inline
+    # constant 0 instead of a register copy of it
+    "-Xclang", "-target-feature", "-Xclang", "-dot13-insts",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I" + INCLUDE, "-I" + CSRC,
 ]
@@ -36,7 +39,8 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
     cmd = [HIPCC] + CFLAGS + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    err = "\n".join(l for l in r.stderr.splitlines()
+                    if "packed-fp32-ops" not in l and "dot13-insts" not in l)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, err))
     if err.strip():

@@ -47,6 +47,14 @@ __device__ __forceinline__ float e4m3_f32_dyn(uint32_t word, int byte) {
     }
 }
 
+// Streaming 16-byte load of weight bytes that are read once per call: the
+// nontemporal hint keeps them from displacing reused data in the caches.
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 __device__ __forceinline__ uint32_t as_u32(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 

@@ -25,6 +25,7 @@ namespace nvfp4 {
 
 constexpr int kMaxValuN = 8;
 constexpr int kMaxKsplit = 8;
+constexpr int kPrefetchMaxN = 4;   // beyond this, double-buffered operands exceed the register file
 
 // Argmax key: order-preserving map of an fp32 value (with -0 folded into +0)
 // in the high word, the complement of the row index in the low word, so the
@@ -69,55 +70,129 @@ __device__ __forceinline__ void mac_step(Frag<N> &f, const uint4 (&c)[kRowPairs]
                 case 2: s = e4m3_f32<2>(sw[r >> 2]); break;
                 default: s = e4m3_f32<3>(sw[r >> 2]); break;
             }
+            // Columns interleaved innermost: N independent dot2 chains.
+            float part[N];
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                float part = dot2(p[0], as_bf16x2(x[n][0]), 0.0f);
+            for (int n = 0; n < N; ++n) part[n] = dot2(p[0], as_bf16x2(x[n][0]), 0.0f);
 #pragma unroll
-                for (int i = 1; i < 8; ++i) part = dot2(p[i], as_bf16x2(x[n][i]), part);
-                f.acc[r][n] = __builtin_fmaf(s, part, f.acc[r][n]);
-            }
+            for (int i = 1; i < 8; ++i)
+#pragma unroll
+                for (int n = 0; n < N; ++n) part[n] = dot2(p[i], as_bf16x2(x[n][i]), part[n]);
+#pragma unroll
+            for (int n = 0; n < N; ++n) f.acc[r][n] = __builtin_fmaf(s, part[n], f.acc[r][n]);
         }
     }
 }
 
-// Sum acc over the 64 lanes.  Four exchange-and-halve rounds over the rows
-// (lane offsets 32, 16, 8, 4) leave each lane one row, then two plain rounds
-// (offsets 2, 1) finish the sum.  Afterwards lane l holds, for every column,
-// the total of row bitrev4(l >> 2); the order of additions is fixed.
+// ------------------------------------------------------- lane reduction
+
+__device__ __forceinline__ void permlane32_swap(float &a, float &b) {
+    // a <- {a[0..31], b[0..31]},  b <- {a[32..63], b[32..63]}
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void permlane16_swap(float &a, float &b) {
+    // a <- {a.row0, b.row0, a.row2, b.row2},  b <- {a.row1, b.row1, a.row3, b.row3}
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+
+constexpr int kDppRowRor8 = 0x128;      // lane l reads lane (l + 8) mod 16 of its row: l ^ 8
+constexpr int kDppHalfMirror = 0x141;   // lane l reads lane 7 - (l mod 8) of its half-row
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]
+
+// Sum acc over the 64 lanes with a fixed tree.  Three exchange-and-halve
+// rounds (lane bit 5 by v_permlane32_swap, bit 4 by v_permlane16_swap, bit 3
+// by a DPP row rotate) and one more against the mirrored half-row leave each
+// lane one row; two DPP quad rounds finish the sum.  Afterwards every lane l
+// holds, for each column, the total of row l >> 2.  The tree is the same for
+// every column and every launch.
 template <int N>
 __device__ __forceinline__ void wave_reduce(Frag<N> &f, int lane) {
 #pragma unroll
-    for (int rnd = 0; rnd < 4; ++rnd) {
-        const int o = 32 >> rnd;
-        const int half = 8 >> rnd;
-        const bool upper = (lane & o) != 0;
+    for (int n = 0; n < N; ++n) {
 #pragma unroll
-        for (int i = 0; i < half; ++i) {
+        for (int i = 0; i < 8; ++i) {
+            permlane32_swap(f.acc[i][n], f.acc[i + 8][n]);
+            f.acc[i][n] = f.acc[i][n] + f.acc[i + 8][n];
+        }
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                const float lo = f.acc[i][n], hi = f.acc[i + half][n];
-                const float send = upper ? lo : hi;
-                const float keep = upper ? hi : lo;
-                f.acc[i][n] = keep + __shfl_xor(send, o);
-            }
+        for (int i = 0; i < 4; ++i) {
+            permlane16_swap(f.acc[i][n], f.acc[i + 4][n]);
+            f.acc[i][n] = f.acc[i][n] + f.acc[i + 4][n];
         }
     }
+    const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        f.acc[0][n] += __shfl_xor(f.acc[0][n], 2);
-        f.acc[0][n] += __shfl_xor(f.acc[0][n], 1);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float lo = f.acc[i][n], hi = f.acc[i + 2][n];
+            const float keep = b3 ? hi : lo, send = b3 ? lo : hi;
+            f.acc[i][n] = keep + dpp<kDppRowRor8>(send);
+        }
+        {
+            const float lo = f.acc[0][n], hi = f.acc[1][n];
+            const float keep = b2 ? hi : lo, send = b2 ? lo : hi;
+            f.acc[0][n] = keep + dpp<kDppHalfMirror>(send);
+        }
+        f.acc[0][n] = f.acc[0][n] + dpp<kDppQuadXor1>(f.acc[0][n]);
+        f.acc[0][n] = f.acc[0][n] + dpp<kDppQuadXor2>(f.acc[0][n]);
     }
 }
 
-__device__ __forceinline__ int reduced_row(int lane) {
-    return ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 2) & 1);
+__device__ __forceinline__ int reduced_row(int lane) { return lane >> 2; }
+
+// One step's operands for one lane: 8 code entries, the scale entry, and the
+// activation pairs of its block for every column.
+template <int N>
+struct StepData {
+    uint4 c[kRowPairs];
+    uint4 sc;
+    uint32_t x[N][8];
+};
+
+template <int N>
+__device__ __forceinline__ void load_step(StepData<N> &d, const uint4 *__restrict__ wq,
+                                          const uint4 *__restrict__ ws, const uint16_t *__restrict__ X,
+                                          int64_t x_stride, int t, int j, int steps, int kb, int lane) {
+    const int64_t entry = int64_t(t) * steps + j;
+    const uint4 *cp = wq + entry * (kRowPairs * kLanes) + lane;
+#pragma unroll
+    for (int q = 0; q < kRowPairs; ++q) d.c[q] = load_stream(cp + q * kLanes);
+    d.sc = load_stream(ws + entry * kLanes + lane);
+    const int b = j * kLanes + lane;
+    if (b < kb) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const uint4 *xp = reinterpret_cast<const uint4 *>(X + n * x_stride + int64_t(b) * kBlock);
+            const uint4 a = xp[0], bb = xp[1];
+            d.x[n][0] = a.x; d.x[n][1] = a.y; d.x[n][2] = a.z; d.x[n][3] = a.w;
+            d.x[n][4] = bb.x; d.x[n][5] = bb.y; d.x[n][6] = bb.z; d.x[n][7] = bb.w;
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) d.x[n][i] = 0u;
+    }
 }
 
 template <int N, bool ARGMAX>
 __global__ void __launch_bounds__(kLanes * kMaxKsplit)
 gemv_valu_kernel(const uint4 *__restrict__ wq, const uint4 *__restrict__ ws, float tscale, int rows,
                  int kb, int steps, int ksplit, const uint16_t *__restrict__ X, int64_t x_stride,
-                 float *__restrict__ Y, int64_t y_stride, unsigned long long *__restrict__ amax_ws) {
+                 float *__restrict__ Y, int64_t y_stride, unsigned long long *__restrict__ amax_ws,
+                 int32_t *__restrict__ argmax_out) {
     __shared__ float red[kMaxKsplit][kTileRows][N];
     const int t = blockIdx.x;
     const int wave = threadIdx.x >> 6;
@@ -131,30 +206,27 @@ gemv_valu_kernel(const uint4 *__restrict__ wq, const uint4 *__restrict__ ws, flo
 #pragma unroll
         for (int n = 0; n < N; ++n) f.acc[r][n] = 0.0f;
 
-    for (int j = j0; j < j1; ++j) {
-        const int64_t entry = int64_t(t) * steps + j;
-        const uint4 *cp = wq + entry * (kRowPairs * kLanes) + lane;
-        uint4 c[kRowPairs];
-#pragma unroll
-        for (int q = 0; q < kRowPairs; ++q) c[q] = cp[q * kLanes];
-        const uint4 sc = ws[entry * kLanes + lane];
-        const int b = j * kLanes + lane;
-        uint32_t x[N][8];
-        if (b < kb) {
-#pragma unroll
-            for (int n = 0; n < N; ++n) {
-                const uint4 *xp = reinterpret_cast<const uint4 *>(X + n * x_stride + int64_t(b) * kBlock);
-                const uint4 a = xp[0], bb = xp[1];
-                x[n][0] = a.x; x[n][1] = a.y; x[n][2] = a.z; x[n][3] = a.w;
-                x[n][4] = bb.x; x[n][5] = bb.y; x[n][6] = bb.z; x[n][7] = bb.w;
-            }
-        } else {
-#pragma unroll
-            for (int n = 0; n < N; ++n)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) x[n][i] = 0u;
+    if constexpr (N <= kPrefetchMaxN) {
+        // Software pipeline over two register buffers: the next step's loads
+        // are in flight while this step's operands are decoded and multiplied.
+        StepData<N> a, b;
+        int j = j0;
+        if (j < j1) load_step<N>(a, wq, ws, X, x_stride, t, j, steps, kb, lane);
+        while (j < j1) {
+            if (j + 1 < j1) load_step<N>(b, wq, ws, X, x_stride, t, j + 1, steps, kb, lane);
+            mac_step<N>(f, a.c, a.sc, a.x);
+            if (++j >= j1) break;
+            if (j + 1 < j1) load_step<N>(a, wq, ws, X, x_stride, t, j + 1, steps, kb, lane);
+            mac_step<N>(f, b.c, b.sc, b.x);
+            ++j;
         }
-        mac_step<N>(f, c, sc, x);
+    } else {
+        // Wider column counts keep one step of operands in registers.
+        for (int j = j0; j < j1; ++j) {
+            StepData<N> cur;
+            load_step<N>(cur, wq, ws, X, x_stride, t, j, steps, kb, lane);
+            mac_step<N>(f, cur.c, cur.sc, cur.x);
+        }
     }
 
     wave_reduce<N>(f, lane);
@@ -189,17 +261,33 @@ gemv_valu_kernel(const uint4 *__restrict__ wq, const uint4 *__restrict__ ws, flo
                 const unsigned long long other = __shfl_xor(key, o);
                 key = other > key ? other : key;
             }
-            if (valid && r == 0) atomicMax(amax_ws + n, key);
+            if (live && r == 0 && key != 0ull)
+                __hip_atomic_fetch_max(amax_ws + n, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-}
-
-__global__ void argmax_init_kernel(unsigned long long *ws, int n) {
-    if (int(threadIdx.x) < n) ws[threadIdx.x] = 0ull;
-}
-
-__global__ void argmax_finish_kernel(const unsigned long long *ws, int n, int32_t *argmax) {
-    if (int(threadIdx.x) < n) argmax[threadIdx.x] = int32_t(0xFFFFFFFFu - uint32_t(ws[threadIdx.x]));
+    if (ARGMAX) {
+        // The last tile to finish turns the keys into row indices and returns
+        // the workspace to all-zero for the next call.  The maxima are
+        // order-independent, so the result does not depend on which tile is
+        // last.  Keys and counter are touched only by device-scope atomics,
+        // which are coherent across the XCDs' L2s without cache maintenance;
+        // waiting for this wave's key atomics to complete before the counter
+        // increment orders them (an agent-scope fence would write back and
+        // invalidate L2 in every tile instead).
+        unsigned int *counter = reinterpret_cast<unsigned int *>(amax_ws + kMaxValuN);
+        __builtin_amdgcn_s_waitcnt(0);
+        unsigned int prev = 0;
+        if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __shfl(prev, 0);
+        if (prev == gridDim.x - 1) {
+            if (lane < N) {
+                const unsigned long long k =
+                    __hip_atomic_exchange(amax_ws + lane, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                argmax_out[lane] = int32_t(0xFFFFFFFFu - uint32_t(k));
+            }
+            if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // ------------------------------------------------------------------ SwiGLU
@@ -231,7 +319,7 @@ inline int choose_ksplit(const Geometry &g) {
 
 template <bool ARGMAX>
 int launch_valu(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
-                int n, float *Y, unsigned long long *amax_ws, hipStream_t stream) {
+                int n, float *Y, unsigned long long *amax_ws, int32_t *argmax_out, hipStream_t stream) {
     const int ksplit = choose_ksplit(g);
     const dim3 grid(unsigned(g.tiles)), block(unsigned(kLanes * ksplit));
     auto q = reinterpret_cast<const uint4 *>(wq);
@@ -240,7 +328,7 @@ int launch_valu(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float t
     const int64_t xs = g.cols, ys = g.rows;
 #define NVFP4_LAUNCH(NN)                                                                            \
     hipLaunchKernelGGL((gemv_valu_kernel<NN, ARGMAX>), grid, block, 0, stream, q, s, tscale, rows, kb, \
-                       steps, ksplit, X, xs, Y, ys, amax_ws)
+                       steps, ksplit, X, xs, Y, ys, amax_ws, argmax_out)
     switch (n) {
         case 1: NVFP4_LAUNCH(1); break;
         case 2: NVFP4_LAUNCH(2); break;
@@ -278,12 +366,13 @@ NVFP4_API int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int
     if (!aligned(Y, 4)) return NVFP4_EALIGN;
     const Geometry g(rows, cols);
     (void)hipGetLastError();
-    if (n <= kMaxValuN) return launch_valu<false>(g, wq, ws, tscale, X, n, Y, nullptr, stream);
+    if (n <= kMaxValuN) return launch_valu<false>(g, wq, ws, tscale, X, n, Y, nullptr, nullptr, stream);
     return launch_mfma(g, wq, ws, tscale, X, n, Y, stream);
 }
 
 NVFP4_API size_t nvfp4_gemv_argmax_workspace_bytes(int n) {
-    return (n >= 1 && n <= kMaxValuN) ? size_t(8) * size_t(n) : 0;
+    // kMaxValuN 64-bit keys and a 32-bit completion counter, whatever n.
+    return (n >= 1 && n <= kMaxValuN) ? size_t(8) * (kMaxValuN + 1) : 0;
 }
 
 NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
@@ -296,13 +385,9 @@ NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tsca
     if (workspace_bytes < nvfp4_gemv_argmax_workspace_bytes(n)) return NVFP4_EWORKSPACE;
     if (rows > int64_t(0x7FFFFFFF)) return NVFP4_ESHAPE;
     const Geometry g(rows, cols);
-    auto *keys = static_cast<unsigned long long *>(workspace);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(argmax_init_kernel, dim3(1), dim3(64), 0, stream, keys, n);
-    if (int st = launch_status()) return st;
-    if (int st = launch_valu<true>(g, wq, ws, tscale, X, n, logits, keys, stream)) return st;
-    hipLaunchKernelGGL(argmax_finish_kernel, dim3(1), dim3(64), 0, stream, keys, n, argmax);
-    return launch_status();
+    return launch_valu<true>(g, wq, ws, tscale, X, n, logits, static_cast<unsigned long long *>(workspace),
+                             argmax, stream);
 }
 
 NVFP4_API int nvfp4_swiglu(const float *gu, int64_t F, int n, uint16_t *h, hipStream_t stream) {

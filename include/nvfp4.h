@@ -129,17 +129,22 @@ int nvfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t ro
 int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
                const uint16_t *X, int n, float *Y, hipStream_t stream);
 
-/* Workspace bytes nvfp4_gemv_argmax needs for n columns (8 * n), 0 if n is
- * out of range. */
+/* Workspace bytes nvfp4_gemv_argmax needs (72: eight 64-bit keys and a
+ * completion counter), 0 if n is out of range. */
 size_t nvfp4_gemv_argmax_workspace_bytes(int n);
 
 /* nvfp4_gemv for 1 <= n <= 8 plus, per column c, argmax[c] = the lowest row
  * index of the largest Y[c][r] (-0 and +0 compare equal) -- the vocabulary
  * projection with the greedy token (bw24 wiki: prefill-argmax vs
  * decode-argmax gate; qwentin README, "How it works": dense-argmax descent).
+ * One kernel launch: every 16-row tile folds its per-column maxima into the
+ * workspace with 64-bit atomic maxima of (order-preserving value key,
+ * complemented row), and the last tile to finish writes argmax.
  * logits [n][rows] may be NULL (not stored).  workspace: device memory of at
- * least nvfp4_gemv_argmax_workspace_bytes(n) bytes, 8-byte aligned, which the
- * call initialises itself; it must not be shared by calls in flight. */
+ * least nvfp4_gemv_argmax_workspace_bytes(n) bytes, 8-byte aligned, that is
+ * all-zero before its first use (e.g. one hipMemset after allocation); every
+ * call leaves it all-zero again.  Calls sharing a workspace must not run
+ * concurrently. */
 int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
                       int64_t cols, const uint16_t *X, int n, float *logits, int32_t *argmax,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);

@@ -56,11 +56,12 @@ def gemv_gpu(wq, ws, tscale, R, K, X: torch.Tensor) -> torch.Tensor:
     return Y
 
 
-def gemv_argmax_gpu(wq, ws, tscale, R, K, X: torch.Tensor, with_logits=True):
+def gemv_argmax_gpu(wq, ws, tscale, R, K, X: torch.Tensor, with_logits=True, workspace=None):
     n = X.shape[0]
     logits = torch.full((n, R), float("nan"), dtype=torch.float32, device=DEV) if with_logits else None
     am = torch.full((n,), -7, dtype=torch.int32, device=DEV)
-    wsp = torch.empty(nv.nvfp4_gemv_argmax_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    wsp = workspace if workspace is not None else torch.zeros(
+        nv.nvfp4_gemv_argmax_workspace_bytes(n), dtype=torch.uint8, device=DEV)
     nv.nvfp4_gemv_argmax(wq, ws, tscale, R, K, X, n, logits, am, wsp)
     return logits, am
 

@@ -68,7 +68,7 @@ def test_plane_sizes_invalid(lib, rows, cols):
 
 
 def test_workspace_bytes(lib):
-    assert [nv.nvfp4_gemv_argmax_workspace_bytes(n) for n in (0, 1, 4, 8, 9)] == [0, 8, 32, 64, 0]
+    assert [nv.nvfp4_gemv_argmax_workspace_bytes(n) for n in (0, 1, 4, 8, 9)] == [0, 72, 72, 72, 0]
 
 
 def test_strerror(lib):
@@ -106,11 +106,11 @@ def test_gemv_validation(lib):
 
 def test_argmax_validation(lib):
     g = lib.nvfp4_gemv_argmax
-    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, B, 31, S0) == EWORKSPACE
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, B, 71, S0) == EWORKSPACE
     assert g(A, B, 1.0, 16, 32, C, 9, NULL, A, B, 1024, S0) == EINVAL   # argmax is n <= 8
-    assert g(A, B, 1.0, 16, 32, C, 4, NULL, NULL, B, 32, S0) == EINVAL
-    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, NULL, 32, S0) == EINVAL
-    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, ctypes.c_void_p(0x200004), 32, S0) == EALIGN
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, NULL, B, 72, S0) == EINVAL
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, NULL, 72, S0) == EINVAL
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, ctypes.c_void_p(0x200004), 72, S0) == EALIGN
 
 
 def test_other_entry_points_validation(lib):
