@@ -11,9 +11,9 @@
 //
 // Work decomposition.  One workgroup per 16-row tile; its `ksplit` waves
 // take contiguous ranges of 64-block steps.  Per step, lane l owns block
-// 64j + l of all 16 rows: 8 code loads of 16 bytes (one per row pair), one
-// 16-byte scale load, and 32 bytes of each activation column, all 128-bit
-// and coalesced across the wave.  The 16 rows reuse the activation registers.
+// 64j + l of all 16 rows: 8 code loads of 16 bytes (one per row pair, each
+// wave load 8 full 128-byte lines), one 16-byte scale load, and 32 bytes of
+// each activation column, all 128-bit and coalesced across the wave.  The 16 rows reuse the activation registers.
 // Decode is one v_cvt_scalef32_pk_bf16_fp4 per 2 codes and one E4M3
 // conversion per row-block, shared by all columns; each column then takes 8
 // v_dot2_f32_bf16 per row-block (products exact in fp32) and one fp32 FMA by
@@ -166,9 +166,11 @@ __device__ __forceinline__ void load_step(StepData<N> &d, const uint4 *__restric
                                           const uint4 *__restrict__ ws, const uint16_t *__restrict__ X,
                                           int64_t x_stride, int t, int j, int steps, int kb, int lane) {
     const int64_t entry = int64_t(t) * steps + j;
-    const uint4 *cp = wq + entry * (kRowPairs * kLanes) + lane;
+    // Entry (t, j, g, q, i) of block 8g + i: lanes 8g..8g+7 read 128
+    // contiguous bytes per row pair.
+    const uint4 *cp = wq + entry * (kRowPairs * kLanes) + (lane >> 3) * 64 + (lane & 7);
 #pragma unroll
-    for (int q = 0; q < kRowPairs; ++q) d.c[q] = load_stream(cp + q * kLanes);
+    for (int q = 0; q < kRowPairs; ++q) d.c[q] = load_stream(cp + q * 8);
     d.sc = load_stream(ws + entry * kLanes + lane);
     const int b = j * kLanes + lane;
     if (b < kb) {

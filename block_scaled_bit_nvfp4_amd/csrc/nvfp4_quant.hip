@@ -88,12 +88,10 @@ __global__ void __launch_bounds__(256) repack_kernel(const uint8_t *__restrict__
     int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t kb = cols / kBlock;
     if (u < code_units) {
-        // u = ((t * steps + j) * 8 + q) * 64 + l
-        int64_t l = u % kLanes, rest = u / kLanes;
-        int64_t q = rest % kRowPairs;
-        rest /= kRowPairs;
-        int64_t j = rest % steps, t = rest / steps;
-        int64_t b = j * kLanes + l;
+        // u = (((t * steps + j) * 8 + g) * 8 + q) * 8 + i, block 64j + 8g + i
+        const int64_t i = u % 8, q = (u / 8) % kRowPairs, grp = (u / 64) % 8, rest = u / 512;
+        const int64_t j = rest % steps, t = rest / steps;
+        const int64_t b = j * kLanes + grp * 8 + i;
         int64_t r0 = t * kTileRows + 2 * q;
         uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
         if (b < kb) {
@@ -130,10 +128,9 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint4 *__restrict__ 
                                                       uint16_t *__restrict__ out_bf16) {
     int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (u >= code_units) return;
-    int64_t l = u % kLanes, rest = u / kLanes;
-    int64_t q = rest % kRowPairs;
-    rest /= kRowPairs;
-    int64_t j = rest % steps, t = rest / steps;
+    const int64_t i = u % 8, q = (u / 8) % kRowPairs, grp = (u / 64) % 8, rest = u / 512;
+    const int64_t j = rest % steps, t = rest / steps;
+    const int64_t l = grp * 8 + i;
     const int64_t b = j * kLanes + l;
     if (b >= cols / kBlock) return;
     const uint4 c = wq[u];

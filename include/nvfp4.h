@@ -31,16 +31,19 @@
  *
  * Repacked layout (what the products read; "split-plane": codes and scales
  * are two separate planes).  Let T = ceil(rows/16) row tiles, KB = cols/16
- * blocks per row, S = ceil(KB/64) steps of 64 blocks.
- *   code plane  uint8 [T][S][8][64][16]: entry (t, j, q, l) holds the 8
- *       canonical code bytes of block b = 64j + l of row 16t + 2q in bytes
- *       0..7 and of row 16t + 2q + 1 in bytes 8..15;
+ * blocks per row, S = ceil(KB/64) steps of 64 blocks; a step's blocks form 8
+ * groups of 8.
+ *   code plane  uint8 [T][S][8][8][8][16]: entry (t, j, g, q, i) holds the 8
+ *       canonical code bytes of block b = 64j + 8g + i of row 16t + 2q in
+ *       bytes 0..7 and of row 16t + 2q + 1 in bytes 8..15;
  *   scale plane uint8 [T][S][64][16]: byte i of entry (t, j, l) is the scale
  *       of block 64j + l of row 16t + i;
  *   positions past the last row or block hold 0.
- * One 64-lane wavefront reads one (t, j, q) code entry as 64 x 16 contiguous
- * bytes and one (t, j) scale entry likewise: 128-bit coalesced loads, each
- * byte once per call for all N columns.
+ * A 64-lane wavefront of the matvec gives lane l block 64j + l: for row pair
+ * q its 64 code entries are 8 full 128-byte lines of the (t, j) region, and
+ * its scale entry (t, j) is 1 KiB contiguous -- 128-bit coalesced loads, each
+ * byte once per call for all N columns.  The wide contraction reads a group
+ * of 8 blocks of a tile as 1 KiB contiguous.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are device memory owned by the caller; the library

@@ -274,10 +274,11 @@ uint16_t oracle_bf16_rne(double v)
 /* Reference of the library's repacked ("split-plane") layout, written from
  * its published definition, not from the library's code.  The definition:
  *   rows are grouped in tiles of 16; blocks (16 elements) of a row are
- *   grouped in steps of 64; T = ceil(R/16), KB = K/16, S = ceil(KB/64);
- *   code plane  [T][S][8][64][16 bytes]: entry (t, j, q, l) holds the 8
- *     canonical code bytes of block b = 64j + l of row 16t + 2q in bytes
- *     0..7 and the same block of row 16t + 2q + 1 in bytes 8..15;
+ *   grouped in steps of 64, and a step's blocks in 8 groups of 8;
+ *   T = ceil(R/16), KB = K/16, S = ceil(KB/64);
+ *   code plane  [T][S][8][8][8][16 bytes]: entry (t, j, g, q, i) holds the 8
+ *     canonical code bytes of block b = 64j + 8g + i of row 16t + 2q in
+ *     bytes 0..7 and the same block of row 16t + 2q + 1 in bytes 8..15;
  *   scale plane [T][S][64][16 bytes]: entry (t, j, l) byte i is the scale
  *     of block 64j + l of row 16t + i;
  *   positions past the last row or block hold 0.
@@ -294,18 +295,19 @@ void oracle_repack(const uint8_t *codes, const uint8_t *scales, int64_t R, int64
         for (int64_t j = 0; j < S; ++j)
             for (int64_t l = 0; l < 64; ++l) {
                 int64_t b = 64 * j + l;
+                int64_t g = l / 8, i = l % 8;
                 if (b >= KB) continue;
                 for (int64_t q = 0; q < 8; ++q)
                     for (int64_t h = 0; h < 2; ++h) {
                         int64_t r = 16 * t + 2 * q + h;
                         if (r >= R) continue;
-                        uint8_t *dst = wq + (((t * S + j) * 8 + q) * 64 + l) * 16 + 8 * h;
+                        uint8_t *dst = wq + ((((t * S + j) * 8 + g) * 8 + q) * 8 + i) * 16 + 8 * h;
                         memcpy(dst, codes + r * (K / 2) + 8 * b, 8);
                     }
-                for (int64_t i = 0; i < 16; ++i) {
-                    int64_t r = 16 * t + i;
+                for (int64_t i16 = 0; i16 < 16; ++i16) {
+                    int64_t r = 16 * t + i16;
                     if (r >= R) continue;
-                    ws[((t * S + j) * 64 + l) * 16 + i] = scales[r * KB + b];
+                    ws[((t * S + j) * 64 + l) * 16 + i16] = scales[r * KB + b];
                 }
             }
 }

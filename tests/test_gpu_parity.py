@@ -150,15 +150,20 @@ def test_gemv_parity(R, K, n, tscale):
     G.assert_within_tolerance(Y, Y_ref, S, "gemv %dx%d n=%d" % (R, K, n))
 
 
-@pytest.mark.parametrize("n", [12, 33])
-def test_gemv_wide_parity(n):
-    R, K = 80, 1024
-    wq, ws, c_ref, s_ref = _prepare(R, K, 77)
-    X = G.seeded_x(n, K, seed=78)
-    G.note("gemv wide n=%d" % n)
+@pytest.mark.parametrize("R,K,n", [
+    (80, 1024, 12), (80, 1024, 33),
+    (1000, 1040, 130),     # ragged rows, a partial k chunk, two column tiles
+    (257, 2064, 9),        # one row past a tile, K not a multiple of 64
+    (17, 16, 300),         # a single block per row
+    (4096, 512, 256),      # several workgroups of full tiles
+])
+def test_gemv_wide_parity(R, K, n):
+    wq, ws, c_ref, s_ref = _prepare(R, K, 77 + R + K)
+    X = G.seeded_x(n, K, seed=78 + n)
+    G.note("gemv wide %dx%d n=%d" % (R, K, n))
     Y = G.gemv_gpu(wq, ws, 1.0, R, K, X).cpu().numpy()
     Y_ref, S = oracle.gemv(c_ref, s_ref, 1.0, G.wl.bf16_bits(X))
-    G.assert_within_tolerance(Y, Y_ref, S, "gemv wide n=%d" % n)
+    G.assert_within_tolerance(Y, Y_ref, S, "gemv wide %dx%d n=%d" % (R, K, n))
 
 
 def test_gemv_exact_special_cases():

@@ -177,14 +177,14 @@ def _unrepack(wq, ws, R, K):
     S = (KB + 63) // 64
     codes = np.zeros((R, K // 2), np.uint8)
     scales = np.zeros((R, KB), np.uint8)
-    cq = wq.reshape(T, S, 8, 64, 2, 8)
+    cq = wq.reshape(T, S, 8, 8, 8, 2, 8)      # [t][j][g][q][i][row of pair][byte]
     sq = ws.reshape(T, S, 64, 16)
     for r in range(R):
         t, q, h = r // 16, (r % 16) // 2, r % 2
         for b in range(KB):
-            j, l = b // 64, b % 64
-            codes[r, 8 * b:8 * b + 8] = cq[t, j, q, l, h]
-            scales[r, b] = sq[t, j, l, r % 16]
+            j, g, i = b // 64, (b % 64) // 8, b % 8
+            codes[r, 8 * b:8 * b + 8] = cq[t, j, g, q, i, h]
+            scales[r, b] = sq[t, j, b % 64, r % 16]
     return codes, scales
 
 
@@ -223,4 +223,4 @@ def test_repack_hand_derived_positions():
             want = scales[int(f[3]), int(f[4])]
         assert plane[off] == want, line
         n += 1
-    assert n == 17
+    assert n == 20
