@@ -266,6 +266,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_4096x4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (read + write), e.g. to "
+                         "calibrate HBM traffic counters against a known byte count")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the NVFP4 matvec path runs on a single MI355X "
@@ -274,6 +277,15 @@ def main():
         sys.exit(2)
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
+    if args.copy_probe_mib:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=DEV)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "launches": 5}))
+        return
     nv.load()
     step = Step(args.workload)
     step.run()
