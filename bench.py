@@ -68,7 +68,7 @@ def gemv_bytes(rows, cols, n):
 class Step:
     """The launches of one pass over a workload, with their algorithmic bytes."""
 
-    def __init__(self, name):
+    def __init__(self, name, fused_mlp=True):
         self.w = wl.WORKLOADS[name]
         w = self.w
         self.n = w.n
@@ -87,14 +87,19 @@ class Step:
             gu_m, dn_m = w.matrices
             self.x = wl.activations(1, gu_m.cols, seed=wl.seed_of(name, "x"), device=DEV)
             self.layers = [(Matrix(w, gu_m, c), Matrix(w, dn_m, c)) for c in range(w.copies)]
-            F = dn_m.cols
+            F, Dh = dn_m.cols, gu_m.cols
             self.gu = torch.empty(1, gu_m.rows, dtype=torch.float32, device=DEV)
             self.h = torch.empty(1, F, dtype=torch.bfloat16, device=DEV)
             self.y = torch.empty(1, dn_m.rows, dtype=torch.float32, device=DEV)
             for G_, D in self.layers:
-                self.launches.append((self._gemv(G_, self.x, 1, self.gu), gemv_bytes(G_.rows, G_.cols, 1),
-                                      2 * G_.rows * G_.cols, "gemv"))
-                self.launches.append((self._swiglu(F), 1 * 2 * F * 4 + F * 2, 4 * F, "swiglu"))
+                if fused_mlp:
+                    # gate||up with SwiGLU in the epilogue (writes h), then down
+                    nbytes = G_.weight_bytes() + 2 * Dh + 2 * F
+                    self.launches.append((self._gemv_swiglu(G_, Dh, F), nbytes, 2 * G_.rows * G_.cols, "gemv"))
+                else:
+                    self.launches.append((self._gemv(G_, self.x, 1, self.gu), gemv_bytes(G_.rows, G_.cols, 1),
+                                          2 * G_.rows * G_.cols, "gemv"))
+                    self.launches.append((self._swiglu(F), 1 * 2 * F * 4 + F * 2, 4 * F, "swiglu"))
                 self.launches.append((self._gemv(D, self.h, 1, self.y), gemv_bytes(D.rows, D.cols, 1),
                                       2 * D.rows * D.cols, "gemv"))
         elif name == "verify_vocab_n4":
@@ -127,6 +132,11 @@ class Step:
     def _gemv(M, x, n, y):
         def f():
             nv.nvfp4_gemv(M.wq, M.ws, M.tscale, M.rows, M.cols, x, n, y)
+        return f
+
+    def _gemv_swiglu(self, G_, Dh, F):
+        def f():
+            nv.nvfp4_gemv_swiglu(G_.wq, G_.ws, G_.tscale, Dh, F, self.x, 1, None, self.h)
         return f
 
     def _swiglu(self, F):
@@ -266,6 +276,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_4096x4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mlp-three-launches", action="store_true",
+                    help="run the decode MLP as gate||up matvec, SwiGLU and down matvec (three launches "
+                         "per layer) instead of gate||up with SwiGLU fused, then down (two launches)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (read + write), e.g. to "
                          "calibrate HBM traffic counters against a known byte count")
@@ -287,7 +300,7 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "launches": 5}))
         return
     nv.load()
-    step = Step(args.workload)
+    step = Step(args.workload, fused_mlp=not args.mlp_three_launches)
     step.run()
     torch.cuda.synchronize()
 
@@ -339,6 +352,9 @@ def main():
             "bytes_per_step": step.bytes, "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "layer_tokens_per_s": round(w.copies * w.n / step_s, 1),
             "timing": "one HIP graph replay per step",
+            "mlp": ("three launches per layer" if args.mlp_three_launches else
+                    "two launches per layer (gate||up with SwiGLU fused, down)")
+            if args.workload == "mlp_27b_decode" else None,
         },
         "roofline": roof,
     }

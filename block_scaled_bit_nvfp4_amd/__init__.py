@@ -20,6 +20,7 @@ __all__ = [
     "nvfp4_strerror", "nvfp4_repacked_code_bytes", "nvfp4_repacked_scale_bytes",
     "nvfp4_quantize", "nvfp4_repack", "nvfp4_dequant", "nvfp4_gemv",
     "nvfp4_gemv_argmax_workspace_bytes", "nvfp4_gemv_argmax", "nvfp4_swiglu",
+    "nvfp4_gemv_swiglu",
     "alloc_repacked",
 ]
 
@@ -64,6 +65,7 @@ def load():
             "nvfp4_gemv_argmax_workspace_bytes": (sz, [i32]),
             "nvfp4_gemv_argmax": (i32, [P, P, f32, i64, i64, P, i32, P, P, P, sz, P]),
             "nvfp4_swiglu": (i32, [P, i64, i32, P, P]),
+            "nvfp4_gemv_swiglu": (i32, [P, P, f32, i64, i64, P, i32, P, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -142,6 +144,11 @@ def nvfp4_gemv_argmax(wq, ws, tscale, rows, cols, X, n, logits, argmax, workspac
 
 def nvfp4_swiglu(gu, F, n, h, stream=None):
     _check(load().nvfp4_swiglu(_ptr(gu), int(F), int(n), _ptr(h), _stream(stream, gu)), "nvfp4_swiglu")
+
+
+def nvfp4_gemv_swiglu(wq_gu, ws_gu, tscale, hidden, F, X, n, gu, h, stream=None):
+    _check(load().nvfp4_gemv_swiglu(_ptr(wq_gu), _ptr(ws_gu), float(tscale), int(hidden), int(F), _ptr(X),
+                                    int(n), _ptr(gu), _ptr(h), _stream(stream, wq_gu)), "nvfp4_gemv_swiglu")
 
 
 def alloc_repacked(rows: int, cols: int, device="cuda"):

@@ -10,184 +10,12 @@
 // the draft tree and the persistent-MLP decode GEMV.
 //
 // Work decomposition.  One workgroup per 16-row tile; its `ksplit` waves
-// take contiguous ranges of 64-block steps.  Per step, lane l owns block
-// 64j + l of all 16 rows: 8 code loads of 16 bytes (one per row pair, each
-// wave load 8 full 128-byte lines), one 16-byte scale load, and 32 bytes of
-// each activation column, all 128-bit and coalesced across the wave.  The 16 rows reuse the activation registers.
-// Decode is one v_cvt_scalef32_pk_bf16_fp4 per 2 codes and one E4M3
-// conversion per row-block, shared by all columns; each column then takes 8
-// v_dot2_f32_bf16 per row-block (products exact in fp32) and one fp32 FMA by
-// the block scale.  The reduction over lanes and waves has a fixed shape that
+// take contiguous ranges of 64-block steps (the per-lane step is described in
+// nvfp4_valu.h).  The reduction over lanes and waves has a fixed shape that
 // depends only on (rows, cols), never on n or on timing.
-#include "nvfp4_host.h"
+#include "nvfp4_valu.h"
 
 namespace nvfp4 {
-
-constexpr int kMaxValuN = 8;
-constexpr int kMaxKsplit = 8;
-constexpr int kPrefetchMaxN = 4;   // beyond this, double-buffered operands exceed the register file
-
-// Argmax key: order-preserving map of an fp32 value (with -0 folded into +0)
-// in the high word, the complement of the row index in the low word, so the
-// unsigned maximum picks the largest value and, among equals, the lowest row.
-__device__ __forceinline__ unsigned long long argmax_key(float y, uint32_t row) {
-    uint32_t b = __float_as_uint(y == 0.0f ? 0.0f : y);
-    uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    return (static_cast<unsigned long long>(k) << 32) | (0xFFFFFFFFu - row);
-}
-
-template <int N>
-struct Frag {
-    float acc[kTileRows][N];
-};
-
-// acc[r][c] += s_r * sum over the block of e2m1 * x_c for the 16 rows of one
-// (tile, step) entry held by this lane.
-template <int N>
-__device__ __forceinline__ void mac_step(Frag<N> &f, const uint4 (&c)[kRowPairs], const uint4 &sc,
-                                         const uint32_t (&x)[N][8]) {
-    const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
-#pragma unroll
-    for (int q = 0; q < kRowPairs; ++q) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int r = 2 * q + h;
-            const uint32_t d0 = h ? c[q].z : c[q].x;
-            const uint32_t d1 = h ? c[q].w : c[q].y;
-            bf16x2 p[8];
-            p[0] = e2m1x2_bf16<0>(d0);
-            p[1] = e2m1x2_bf16<1>(d0);
-            p[2] = e2m1x2_bf16<2>(d0);
-            p[3] = e2m1x2_bf16<3>(d0);
-            p[4] = e2m1x2_bf16<0>(d1);
-            p[5] = e2m1x2_bf16<1>(d1);
-            p[6] = e2m1x2_bf16<2>(d1);
-            p[7] = e2m1x2_bf16<3>(d1);
-            float s;
-            switch (r & 3) {
-                case 0: s = e4m3_f32<0>(sw[r >> 2]); break;
-                case 1: s = e4m3_f32<1>(sw[r >> 2]); break;
-                case 2: s = e4m3_f32<2>(sw[r >> 2]); break;
-                default: s = e4m3_f32<3>(sw[r >> 2]); break;
-            }
-            // Columns interleaved innermost: N independent dot2 chains.
-            float part[N];
-#pragma unroll
-            for (int n = 0; n < N; ++n) part[n] = dot2(p[0], as_bf16x2(x[n][0]), 0.0f);
-#pragma unroll
-            for (int i = 1; i < 8; ++i)
-#pragma unroll
-                for (int n = 0; n < N; ++n) part[n] = dot2(p[i], as_bf16x2(x[n][i]), part[n]);
-#pragma unroll
-            for (int n = 0; n < N; ++n) f.acc[r][n] = __builtin_fmaf(s, part[n], f.acc[r][n]);
-        }
-    }
-}
-
-// ------------------------------------------------------- lane reduction
-
-__device__ __forceinline__ void permlane32_swap(float &a, float &b) {
-    // a <- {a[0..31], b[0..31]},  b <- {a[32..63], b[32..63]}
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ void permlane16_swap(float &a, float &b) {
-    // a <- {a.row0, b.row0, a.row2, b.row2},  b <- {a.row1, b.row1, a.row3, b.row3}
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-
-template <int Ctrl>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
-}
-
-constexpr int kDppRowRor8 = 0x128;      // lane l reads lane (l + 8) mod 16 of its row: l ^ 8
-constexpr int kDppHalfMirror = 0x141;   // lane l reads lane 7 - (l mod 8) of its half-row
-constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1, 0, 3, 2]
-constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2, 3, 0, 1]
-
-// Sum acc over the 64 lanes with a fixed tree.  Three exchange-and-halve
-// rounds (lane bit 5 by v_permlane32_swap, bit 4 by v_permlane16_swap, bit 3
-// by a DPP row rotate) and one more against the mirrored half-row leave each
-// lane one row; two DPP quad rounds finish the sum.  Afterwards every lane l
-// holds, for each column, the total of row l >> 2.  The tree is the same for
-// every column and every launch.
-template <int N>
-__device__ __forceinline__ void wave_reduce(Frag<N> &f, int lane) {
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            permlane32_swap(f.acc[i][n], f.acc[i + 8][n]);
-            f.acc[i][n] = f.acc[i][n] + f.acc[i + 8][n];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            permlane16_swap(f.acc[i][n], f.acc[i + 4][n]);
-            f.acc[i][n] = f.acc[i][n] + f.acc[i + 4][n];
-        }
-    }
-    const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const float lo = f.acc[i][n], hi = f.acc[i + 2][n];
-            const float keep = b3 ? hi : lo, send = b3 ? lo : hi;
-            f.acc[i][n] = keep + dpp<kDppRowRor8>(send);
-        }
-        {
-            const float lo = f.acc[0][n], hi = f.acc[1][n];
-            const float keep = b2 ? hi : lo, send = b2 ? lo : hi;
-            f.acc[0][n] = keep + dpp<kDppHalfMirror>(send);
-        }
-        f.acc[0][n] = f.acc[0][n] + dpp<kDppQuadXor1>(f.acc[0][n]);
-        f.acc[0][n] = f.acc[0][n] + dpp<kDppQuadXor2>(f.acc[0][n]);
-    }
-}
-
-__device__ __forceinline__ int reduced_row(int lane) { return lane >> 2; }
-
-// One step's operands for one lane: 8 code entries, the scale entry, and the
-// activation pairs of its block for every column.
-template <int N>
-struct StepData {
-    uint4 c[kRowPairs];
-    uint4 sc;
-    uint32_t x[N][8];
-};
-
-template <int N>
-__device__ __forceinline__ void load_step(StepData<N> &d, const uint4 *__restrict__ wq,
-                                          const uint4 *__restrict__ ws, const uint16_t *__restrict__ X,
-                                          int64_t x_stride, int t, int j, int steps, int kb, int lane) {
-    const int64_t entry = int64_t(t) * steps + j;
-    // Entry (t, j, g, q, i) of block 8g + i: lanes 8g..8g+7 read 128
-    // contiguous bytes per row pair.
-    const uint4 *cp = wq + entry * (kRowPairs * kLanes) + (lane >> 3) * 64 + (lane & 7);
-#pragma unroll
-    for (int q = 0; q < kRowPairs; ++q) d.c[q] = load_stream(cp + q * 8);
-    d.sc = load_stream(ws + entry * kLanes + lane);
-    const int b = j * kLanes + lane;
-    if (b < kb) {
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const uint4 *xp = reinterpret_cast<const uint4 *>(X + n * x_stride + int64_t(b) * kBlock);
-            const uint4 a = xp[0], bb = xp[1];
-            d.x[n][0] = a.x; d.x[n][1] = a.y; d.x[n][2] = a.z; d.x[n][3] = a.w;
-            d.x[n][4] = bb.x; d.x[n][5] = bb.y; d.x[n][6] = bb.z; d.x[n][7] = bb.w;
-        }
-    } else {
-#pragma unroll
-        for (int n = 0; n < N; ++n)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) d.x[n][i] = 0u;
-    }
-}
 
 template <int N, bool ARGMAX>
 __global__ void __launch_bounds__(kLanes * kMaxKsplit)
@@ -203,33 +31,8 @@ gemv_valu_kernel(const uint4 *__restrict__ wq, const uint4 *__restrict__ ws, flo
     const int j1 = (steps * (wave + 1)) / ksplit;
 
     Frag<N> f;
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r)
-#pragma unroll
-        for (int n = 0; n < N; ++n) f.acc[r][n] = 0.0f;
-
-    if constexpr (N <= kPrefetchMaxN) {
-        // Software pipeline over two register buffers: the next step's loads
-        // are in flight while this step's operands are decoded and multiplied.
-        StepData<N> a, b;
-        int j = j0;
-        if (j < j1) load_step<N>(a, wq, ws, X, x_stride, t, j, steps, kb, lane);
-        while (j < j1) {
-            if (j + 1 < j1) load_step<N>(b, wq, ws, X, x_stride, t, j + 1, steps, kb, lane);
-            mac_step<N>(f, a.c, a.sc, a.x);
-            if (++j >= j1) break;
-            if (j + 1 < j1) load_step<N>(a, wq, ws, X, x_stride, t, j + 1, steps, kb, lane);
-            mac_step<N>(f, b.c, b.sc, b.x);
-            ++j;
-        }
-    } else {
-        // Wider column counts keep one step of operands in registers.
-        for (int j = j0; j < j1; ++j) {
-            StepData<N> cur;
-            load_step<N>(cur, wq, ws, X, x_stride, t, j, steps, kb, lane);
-            mac_step<N>(f, cur.c, cur.sc, cur.x);
-        }
-    }
+    clear(f);
+    accumulate_steps<N>(f, wq, ws, X, x_stride, t, j0, j1, steps, kb, lane);
 
     wave_reduce<N>(f, lane);
     if ((lane & 3) == 0) {
@@ -294,35 +97,81 @@ gemv_valu_kernel(const uint4 *__restrict__ wq, const uint4 *__restrict__ ws, flo
 
 // ------------------------------------------------------------------ SwiGLU
 
+// SiLU(g) * u in fp32 and its nearest-even bf16 bits; the one definition the
+// separate SwiGLU kernel and the fused gate||up kernel share.
+__device__ __forceinline__ float swiglu_f32(float g, float u) { return g * u / (1.0f + expf(-g)); }
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
+    const uint32_t b = __float_as_uint(v);
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;     // finite v
+}
+
 __global__ void __launch_bounds__(256) swiglu_kernel(const float *__restrict__ gu, int64_t F, int64_t total,
                                                      uint16_t *__restrict__ h) {
     int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= total) return;
     const int64_t n = i / F, c = i % F;
-    const float g = gu[n * 2 * F + c];
-    const float u = gu[n * 2 * F + F + c];
-    const float v = g * u / (1.0f + expf(-g));
-    const uint32_t b = __float_as_uint(v);
-    h[i] = uint16_t((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);   // nearest-even (finite v)
+    h[i] = uint16_t(bf16_rne_bits(swiglu_f32(gu[n * 2 * F + c], gu[n * 2 * F + F + c])));
+}
+
+// The gate||up product with SwiGLU in its epilogue: one workgroup per pair
+// (gate tile p, up tile p + F/16) of the stacked [2F][K] matrix, `ksplit`
+// waves per tile with the k split the plain matvec uses for that matrix, so
+// gu and h carry the bits of nvfp4_gemv followed by nvfp4_swiglu; the fp32
+// gate/up values never travel through memory unless asked for.
+// Up to 16 waves (k split 8) at one column, whose matvec fits 128 registers;
+// up to 8 waves (k split 4) otherwise.
+template <int N>
+constexpr int swiglu_max_waves() { return N == 1 ? 2 * kMaxKsplit : kMaxKsplit; }
+
+template <int N>
+__global__ void __launch_bounds__(kLanes * swiglu_max_waves<N>())
+gemv_swiglu_kernel(const uint4 *__restrict__ wq, const uint4 *__restrict__ ws, float tscale, int F, int kb,
+                   int steps, int ksplit, const uint16_t *__restrict__ X, int64_t x_stride,
+                   float *__restrict__ gu_out, uint16_t *__restrict__ h) {
+    __shared__ float red[2 * kMaxKsplit][kTileRows][N];
+    const int pair = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int half = wave / ksplit, part = wave % ksplit;       // half 0: gate, 1: up
+    const int t = pair + half * (F / kTileRows);
+    const int j0 = (steps * part) / ksplit;
+    const int j1 = (steps * (part + 1)) / ksplit;
+
+    Frag<N> f;
+    clear(f);
+    accumulate_steps<N>(f, wq, ws, X, x_stride, t, j0, j1, steps, kb, lane);
+    wave_reduce<N>(f, lane);
+    if ((lane & 3) == 0) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) red[wave][reduced_row(lane)][n] = f.acc[0][n];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    for (int idx = lane; idx < kTileRows * N; idx += kLanes) {
+        const int n = idx / kTileRows, r = idx % kTileRows;
+        float g = red[0][r][n], u = red[ksplit][r][n];
+        for (int w = 1; w < ksplit; ++w) {
+            g += red[w][r][n];
+            u += red[ksplit + w][r][n];
+        }
+        g *= tscale;
+        u *= tscale;
+        const int row = pair * kTileRows + r;
+        if (gu_out) {
+            gu_out[int64_t(n) * 2 * F + row] = g;
+            gu_out[int64_t(n) * 2 * F + F + row] = u;
+        }
+        h[int64_t(n) * F + row] = uint16_t(bf16_rne_bits(swiglu_f32(g, u)));
+    }
 }
 
 // ------------------------------------------------------------------ dispatch
 
-// Waves per tile: enough (tile, part) waves to give every CU several, never
-// more parts than steps.  Depends only on the matrix shape.
-inline int choose_ksplit(const Geometry &g) {
-    const int64_t target_waves = 2048;
-    int64_t k = ceil_div(target_waves, g.tiles);
-    if (k > g.steps) k = g.steps;
-    if (k > kMaxKsplit) k = kMaxKsplit;
-    if (k < 1) k = 1;
-    return int(k);
-}
-
 template <bool ARGMAX>
 int launch_valu(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
                 int n, float *Y, unsigned long long *amax_ws, int32_t *argmax_out, hipStream_t stream) {
-    const int ksplit = choose_ksplit(g);
+    const int ksplit = choose_ksplit(g.tiles, g.steps);
     const dim3 grid(unsigned(g.tiles)), block(unsigned(kLanes * ksplit));
     auto q = reinterpret_cast<const uint4 *>(wq);
     auto s = reinterpret_cast<const uint4 *>(ws);
@@ -348,6 +197,42 @@ int launch_valu(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float t
 
 int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
                 int n, float *Y, hipStream_t stream);
+
+int launch_gemv_swiglu(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t hidden, int64_t F,
+                       const uint16_t *X, int n, float *gu, uint16_t *h, hipStream_t stream) {
+    const Geometry g(2 * F, hidden);
+    const int ksplit = choose_ksplit(g.tiles, g.steps);
+    const int max_waves = n == 1 ? swiglu_max_waves<1>() : swiglu_max_waves<2>();
+    if (2 * ksplit > max_waves) {
+        // Narrow MLPs (F < 4096) over a wide hidden dimension split k further
+        // than one workgroup can hold for n > 1: the plain matvec into gu,
+        // then the SwiGLU kernel, give the same bits.
+        if (!gu) return NVFP4_ESHAPE;
+        if (int st = launch_valu<false>(g, wq, ws, tscale, X, n, gu, nullptr, nullptr, stream)) return st;
+        hipLaunchKernelGGL(swiglu_kernel, dim3(unsigned(ceil_div(F * n, 256))), dim3(256), 0, stream, gu, F,
+                           F * n, h);
+        return launch_status();
+    }
+    const dim3 grid(unsigned(F / kTileRows)), block(unsigned(kLanes * 2 * ksplit));
+    auto q = reinterpret_cast<const uint4 *>(wq);
+    auto s = reinterpret_cast<const uint4 *>(ws);
+#define NVFP4_LAUNCH(NN)                                                                                   \
+    hipLaunchKernelGGL(gemv_swiglu_kernel<NN>, grid, block, 0, stream, q, s, tscale, int(F), int(g.kb), \
+                       int(g.steps), ksplit, X, int64_t(hidden), gu, h)
+    switch (n) {
+        case 1: NVFP4_LAUNCH(1); break;
+        case 2: NVFP4_LAUNCH(2); break;
+        case 3: NVFP4_LAUNCH(3); break;
+        case 4: NVFP4_LAUNCH(4); break;
+        case 5: NVFP4_LAUNCH(5); break;
+        case 6: NVFP4_LAUNCH(6); break;
+        case 7: NVFP4_LAUNCH(7); break;
+        case 8: NVFP4_LAUNCH(8); break;
+        default: return NVFP4_EINVAL;
+    }
+#undef NVFP4_LAUNCH
+    return launch_status();
+}
 
 }  // namespace nvfp4
 
@@ -390,6 +275,18 @@ NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tsca
     (void)hipGetLastError();
     return launch_valu<true>(g, wq, ws, tscale, X, n, logits, static_cast<unsigned long long *>(workspace),
                              argmax, stream);
+}
+
+NVFP4_API int nvfp4_gemv_swiglu(const uint8_t *wq_gu, const uint8_t *ws_gu, float tscale, int64_t hidden,
+                                int64_t F, const uint16_t *X, int n, float *gu, uint16_t *h,
+                                hipStream_t stream) {
+    if (!h) return NVFP4_EINVAL;
+    if (F < kTileRows || F % kTileRows != 0) return NVFP4_ESHAPE;
+    if (int st = check_product_args(wq_gu, ws_gu, tscale, 2 * F, hidden, X, n)) return st;
+    if (n > kMaxValuN) return NVFP4_EINVAL;
+    if (!aligned(gu, 4) || !aligned(h, 2)) return NVFP4_EALIGN;
+    (void)hipGetLastError();
+    return launch_gemv_swiglu(wq_gu, ws_gu, tscale, hidden, F, X, n, gu, h, stream);
 }
 
 NVFP4_API int nvfp4_swiglu(const float *gu, int64_t F, int n, uint16_t *h, hipStream_t stream) {

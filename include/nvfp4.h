@@ -160,6 +160,20 @@ int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_
  * F >= 1; gu 16-byte aligned, h 4-byte aligned. */
 int nvfp4_swiglu(const float *gu, int64_t F, int n, uint16_t *h, hipStream_t stream);
 
+/* The gate||up product of a decode MLP with SwiGLU in its epilogue, one
+ * launch: for the stacked [2F][hidden] matrix (gate rows 0..F-1, up rows
+ * F..2F-1), h[c][i] = bf16_nearest_even(SiLU(g) * u) in fp32 with
+ * g = Y[c][i], u = Y[c][F + i] of nvfp4_gemv on that matrix.  gu, when not
+ * NULL, receives Y itself (fp32 [n][2F]); h is bf16 [n][F].  Both are bit for
+ * bit what nvfp4_gemv followed by nvfp4_swiglu give (the pages'
+ * persistent-MLP decode GEMV, qwentin README "How it works", also keeps the
+ * MLP's intermediate out of memory).  1 <= n <= 8; F a multiple of 16;
+ * gu 4-byte and h 2-byte aligned.  One launch whenever n == 1 or F >= 4096 or
+ * hidden <= 4096; other shapes run the plain product into gu (then required,
+ * else NVFP4_ESHAPE) and the SwiGLU kernel, with the same bits. */
+int nvfp4_gemv_swiglu(const uint8_t *wq_gu, const uint8_t *ws_gu, float tscale, int64_t hidden,
+                      int64_t F, const uint16_t *X, int n, float *gu, uint16_t *h, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

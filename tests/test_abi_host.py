@@ -126,3 +126,14 @@ def test_other_entry_points_validation(lib):
     assert lib.nvfp4_swiglu(A, 0, 1, B, S0) == ESHAPE
     assert lib.nvfp4_swiglu(A, 16, 0, B, S0) == EINVAL
     assert lib.nvfp4_swiglu(MIS, 16, 1, B, S0) == EALIGN
+
+
+def test_gemv_swiglu_validation(lib):
+    f = lib.nvfp4_gemv_swiglu
+    assert f(A, B, 1.0, 512, 1024, C, 1, NULL, NULL, S0) == EINVAL      # h
+    assert f(A, B, 1.0, 512, 1000, C, 1, NULL, A, S0) == ESHAPE         # F % 16
+    assert f(A, B, 1.0, 40, 1024, C, 1, NULL, A, S0) == ESHAPE          # hidden % 16
+    assert f(A, B, 1.0, 512, 1024, C, 9, NULL, A, S0) == EINVAL         # n > 8
+    assert f(A, B, 0.0, 512, 1024, C, 1, NULL, A, S0) == EINVAL
+    assert f(MIS, B, 1.0, 512, 1024, C, 1, NULL, A, S0) == EALIGN
+    assert f(A, B, 1.0, 512, 1024, C, 1, ctypes.c_void_p(0x100002), A, S0) == EALIGN

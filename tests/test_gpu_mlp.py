@@ -1,0 +1,86 @@
+"""The fused gate||up + SwiGLU product against the same step as two
+launches (matvec, then SwiGLU), bit for bit, and the decode MLP layer built
+on it against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_bit_nvfp4_amd import workloads as wl
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_scaled_bit_nvfp4_amd as nv
+    nv.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _stacked(D, F, seed):
+    W = wl.weights(2 * F, D, seed=seed, device=G.DEV)
+    c, s = G.quantize_gpu(W)
+    q, ss = G.repack_gpu(c, s, 2 * F, D)
+    return W, q, ss
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int32 if t.element_size() == 4 else torch.int16)
+
+
+@pytest.mark.parametrize("D,F,n", [(512, 1024, 1), (1040, 2064, 2), (96, 48, 3), (5120, 17408, 1),
+                                   (5120, 17408, 4), (4096, 1024, 8), (8192, 1024, 1), (8192, 1024, 2)])
+def test_gemv_swiglu_equals_two_launches(D, F, n):
+    import block_scaled_bit_nvfp4_amd as nv
+    _, q, ss = _stacked(D, F, seed=D + F)
+    X = wl.activations(n, D, seed=n + 5, device=G.DEV)
+    G.note("gemv_swiglu D=%d F=%d n=%d" % (D, F, n))
+    gu = torch.full((n, 2 * F), float("nan"), dtype=torch.float32, device=G.DEV)
+    h = torch.zeros(n, F, dtype=torch.bfloat16, device=G.DEV)
+    nv.nvfp4_gemv_swiglu(q, ss, 0.75, D, F, X, n, gu, h)
+    gu_r = G.gemv_gpu(q, ss, 0.75, 2 * F, D, X)
+    h_r = torch.empty(n, F, dtype=torch.bfloat16, device=G.DEV)
+    nv.nvfp4_swiglu(gu_r, F, n, h_r)
+    assert torch.equal(_bits(gu), _bits(gu_r))
+    assert torch.equal(_bits(h), _bits(h_r))
+    h2 = torch.zeros(n, F, dtype=torch.bfloat16, device=G.DEV)       # without the gu output
+    if n == 1 or F >= 4096 or D <= 4096:
+        nv.nvfp4_gemv_swiglu(q, ss, 0.75, D, F, X, n, None, h2)
+        assert torch.equal(_bits(h2), _bits(h_r))
+    else:
+        with pytest.raises(nv.NVFP4Error):
+            nv.nvfp4_gemv_swiglu(q, ss, 0.75, D, F, X, n, None, h2)
+
+
+def test_mlp_layer_vs_oracle_at_27b_shape():
+    """gate||up+SwiGLU then down, as the decode MLP bench runs it, checked
+    stage by stage against the oracle (the down product on the GPU's own h)."""
+    import block_scaled_bit_nvfp4_amd as nv
+    w = wl.WORKLOADS["mlp_27b_decode"]
+    gate_up, down = w.matrices
+    D, F = gate_up.cols, down.cols
+    W1, q1, s1 = _stacked(D, F, seed=31)
+    W2 = wl.weights(D, F, seed=32, device=G.DEV)
+    c2, t2 = G.quantize_gpu(W2)
+    q2, s2 = G.repack_gpu(c2, t2, D, F)
+    X = wl.activations(1, D, seed=11, device=G.DEV)
+    gu = torch.empty(1, 2 * F, dtype=torch.float32, device=G.DEV)
+    h = torch.empty(1, F, dtype=torch.bfloat16, device=G.DEV)
+    G.note("mlp layer vs oracle")
+    nv.nvfp4_gemv_swiglu(q1, s1, 1.0, D, F, X, 1, gu, h)
+    y = G.gemv_gpu(q2, s2, 1.0, D, F, h).cpu().numpy()
+    rows = np.array(sorted(set(range(16)) | set(range(F - 16, F)) | set(range(4000, 4100))), np.int64)
+    rows_gu = np.concatenate([rows, rows + F])
+    c1r, s1r = oracle.quantize(W1[torch.as_tensor(rows_gu, device=G.DEV)].cpu().numpy())
+    Y1, S1 = oracle.gemv_rows(c1r, s1r, 1.0, wl.bf16_bits(X))
+    G.assert_within_tolerance(gu.cpu().numpy()[:, rows_gu], Y1, S1, "gate||up")
+    from tests.test_gpu_parity import _check_swiglu
+    _check_swiglu(gu.cpu().numpy(), wl.bf16_bits(h))
+    c2r, s2r = oracle.quantize(W2.cpu().numpy())
+    Y2, S2 = oracle.gemv(c2r, s2r, 1.0, wl.bf16_bits(h))
+    G.assert_within_tolerance(y, Y2, S2, "down")
