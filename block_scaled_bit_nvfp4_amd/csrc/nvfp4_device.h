@@ -14,21 +14,42 @@
 namespace nvfp4 {
 
 // Repacked ("split-plane") layout; the public definition is in nvfp4.h.
-constexpr int kTileRows = 16;   // rows per tile
-constexpr int kRowPairs = 8;    // row pairs per tile
-constexpr int kLanes = 64;      // blocks per step (one per lane of a wave64)
-constexpr int kBlock = 16;      // elements per scale block
+constexpr int kBlock = 16;                            // elements per scale block
+constexpr int kTileRows = 16;                         // rows per tile
+constexpr int kSuperTiles = 4;                        // tiles per super-tile
+constexpr int kSuperRows = kTileRows * kSuperTiles;   // 64
+constexpr int kOctet = 8;                             // blocks per octet
+constexpr int kLanes = 64;
+constexpr int kCodeChunk = kLanes * 16;               // one tile's octet of codes: 1 KiB
+constexpr int kScaleChunk = kTileRows * kOctet;       // one tile's octet of scales: 128 B
+constexpr int kCodeRegion = kSuperTiles * kCodeChunk;     // one super-tile's octet: 4 KiB
+constexpr int kScaleRegion = kSuperTiles * kScaleChunk;   // 512 B
 
 typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Two E2M1 codes (byte `Byte` of `word`, element 2i in the low nibble) -> two
-// exact bf16 values packed low/high.  v_cvt_scalef32_pk_bf16_fp4 with scale
-// 1.0; every E2M1 value is a bf16 value, so the conversion is exact.
+// Two E2M1 codes (byte `Byte` of `word`, the even element in the low nibble)
+// -> two exact bf16 values packed low/high.  v_cvt_scalef32_pk_bf16_fp4 with
+// scale 1.0; every E2M1 value is a bf16 value, so the conversion is exact.
 template <int Byte>
 __device__ __forceinline__ bf16x2 e2m1x2_bf16(uint32_t word) {
     return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, Byte);
+}
+
+// Eight E2M1 codes (one 32-bit word, element 0 in the lowest nibble) -> the
+// eight exact bf16 values of an MFMA operand, in element order.
+__device__ __forceinline__ bf16x8 e2m1x8_bf16(uint32_t word) {
+    const bf16x2 p0 = e2m1x2_bf16<0>(word), p1 = e2m1x2_bf16<1>(word);
+    const bf16x2 p2 = e2m1x2_bf16<2>(word), p3 = e2m1x2_bf16<3>(word);
+    bf16x8 o;
+    o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1];
+    o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
+    return o;
 }
 
 // E4M3 byte `Byte` of `word` -> exact fp32 (OCP E4M3 on gfx950: bias 7,
@@ -47,21 +68,29 @@ __device__ __forceinline__ float e4m3_f32_dyn(uint32_t word, int byte) {
     }
 }
 
-// Streaming 16-byte load of weight bytes that are read once per call: the
-// nontemporal hint keeps them from displacing reused data in the caches.
-__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 __device__ __forceinline__ uint32_t as_u32(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// acc + a.lo*b.lo + a.hi*b.hi in fp32 (v_dot2_f32_bf16).  Each product of an
-// E2M1 value and a bf16 value is exact in fp32.
-__device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float acc) {
-    return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+// v holds item g in lane group g (lanes 16g .. 16g + 15); returns o[k] = item
+// k in every lane.  One v_permlane32_swap and two v_permlane16_swap.
+__device__ __forceinline__ void gather_lane_groups(uint32_t v, uint32_t (&o)[4]) {
+    const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);      // (v0 v1 v0 v1), (v2 v3 v2 v3)
+    const auto b0 = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);   // (v0 ...), (v1 ...)
+    const auto b1 = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);   // (v2 ...), (v3 ...)
+    o[0] = b0[0];
+    o[1] = b0[1];
+    o[2] = b1[0];
+    o[3] = b1[1];
+}
+
+// Buffer loads: offsets past the resource's byte count read zeros without a
+// memory access, which bounds every prefetch and ragged tail without a branch.
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9 raw buffer, 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kStream = 2;               // nontemporal: weight bytes are read once per call
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, int(bytes), kRsrcWord3);
 }
 
 }  // namespace nvfp4

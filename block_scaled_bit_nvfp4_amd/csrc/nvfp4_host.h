@@ -18,7 +18,7 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 // 64-bit offsets and 32-bit tile/block counts.
 inline int check_shape(int64_t rows, int64_t cols) {
     if (rows < 1 || cols < 16 || cols % 16 != 0) return NVFP4_ESHAPE;
-    if (rows > (int64_t(1) << 31) - 16 || cols > (int64_t(1) << 31) - 1024) return NVFP4_ESHAPE;
+    if (rows > (int64_t(1) << 31) - 64 || cols > (int64_t(1) << 31) - 1024) return NVFP4_ESHAPE;
     if (rows > (int64_t(1) << 62) / cols) return NVFP4_ESHAPE;
     return NVFP4_OK;
 }
@@ -27,14 +27,15 @@ inline bool tscale_ok(float t) { return t > 0.0f && t <= 3.4028234663852886e38f;
 
 struct Geometry {
     int64_t rows, cols;
-    int64_t kb;     // 16-element blocks per row
-    int64_t tiles;  // 16-row tiles
-    int64_t steps;  // steps of 64 blocks
+    int64_t kb;          // 16-element blocks per row
+    int64_t tiles;       // 16-row tiles
+    int64_t supertiles;  // 64-row super-tiles
+    int64_t octets;      // octets of 8 blocks per row
     Geometry(int64_t r, int64_t c)
         : rows(r), cols(c), kb(c / kBlock), tiles(ceil_div(r, kTileRows)),
-          steps(ceil_div(c / kBlock, kLanes)) {}
-    size_t code_bytes() const { return size_t(tiles) * size_t(steps) * kRowPairs * kLanes * 16; }
-    size_t scale_bytes() const { return size_t(tiles) * size_t(steps) * kLanes * 16; }
+          supertiles(ceil_div(ceil_div(r, kTileRows), kSuperTiles)), octets(ceil_div(c / kBlock, kOctet)) {}
+    size_t code_bytes() const { return size_t(supertiles) * size_t(octets) * kCodeRegion; }
+    size_t scale_bytes() const { return size_t(supertiles) * size_t(octets) * kScaleRegion; }
 };
 
 inline int launch_status() {

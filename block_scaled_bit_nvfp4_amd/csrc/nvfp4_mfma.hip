@@ -11,19 +11,16 @@
 // multiplied on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the tensor
 // scale multiplies the result.
 //
-// Tiling.  A wave owns 64 weight rows x 64 activation columns (64 fp32
-// accumulators per lane) over the whole K; a workgroup's four waves share one
-// 64-column tile of X, staged through LDS in 128-deep k chunks (double
-// buffered), and take four different 64-row units.  Weights never touch LDS:
-// every lane loads whole 16-byte code entries of the repacked layout (two rows
-// x one 16-element block) and decodes them in registers; a chunk is one group
-// of 8 blocks, 1 KiB contiguous per tile.  The contraction is free to permute
-// k and the output rows, so each 16-byte entry feeds four MFMA operands
-// directly: MFMA (h, e) takes row 2q + h of the entry's row pair and elements
-// 8e..8e+7 of its block, and lane group s of the wave (lanes 16s .. 16s + 15)
-// takes blocks s and s + 4 of the group.  The activation operand is read from
-// LDS with the same k mapping.  A lane's outputs come out as 8 consecutive
-// rows of one column.
+// Tiling.  A wave owns one 64-row super-tile x 64 activation columns (64
+// fp32 accumulators per lane) over the whole K; a workgroup's four waves
+// share one 64-column tile of X, staged through LDS in octet chunks of 128 k
+// (double buffered), and take four different super-tiles.  Weights never
+// touch LDS: per octet a lane loads its 16-byte code entry of each of the
+// four tiles and its one 8-byte scale entry (spread to the other lane groups
+// with v_permlane swaps), and decodes in registers: word d of a tile's entry
+// is directly the A operand of k = 128o + 32d .. +31 (lane 16g + r: row r,
+// elements 8g .. 8g + 7).  A lane's outputs come out as 4 consecutive rows of
+// one column per tile.
 #include "nvfp4_host.h"
 
 namespace nvfp4 {
@@ -32,11 +29,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmWaves = 4;         // waves per workgroup
-constexpr int kGemmUnitTiles = 4;     // 16-row tiles per wave: 64 weight rows
 constexpr int kGemmCols = 64;         // activation columns per workgroup
 constexpr int kGemmColSub = kGemmCols / 16;
-constexpr int kChunkBlocks = 8;       // a chunk is one group of 8 blocks
-constexpr int kChunkK = kChunkBlocks * kBlock;
+constexpr int kChunkK = kOctet * kBlock;   // a chunk is one octet: 128 k
 constexpr int kLdsRowBytes = kChunkK * 2 + 16;   // padded: 16-byte reads of
                                                  // neighbouring columns spread
                                                  // over the banks
@@ -62,58 +57,43 @@ __device__ __forceinline__ bf16x8_t decode_a(uint32_t word, float s) {
     return out;
 }
 
-// One chunk of this lane's weights: [tile pair tp][half f] entries for
-// blocks 4f + s of the group, and their two scale bytes (rows 2q, 2q + 1).
+// One chunk (octet) of this lane's weights: its code entry of each tile of
+// the super-tile and its scale entry (tile lane >> 4, row lane & 15).
 struct AFrag {
-    uint4 code[2][2];
-    uint32_t scale[2][2];
+    uint4 code[kSuperTiles];
+    uint2 scale;
 };
 
 __global__ void __launch_bounds__(kGemmWaves * kLanes, 2)
-gemm_mfma_kernel(const uint4 *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows,
-                 int tiles, int steps, int chunks, int K, const uint16_t *__restrict__ X, int n,
+gemm_mfma_kernel(const uint4 *__restrict__ wq, const uint2 *__restrict__ ws, float tscale, int rows,
+                 int supertiles, int octets, int chunks, int K, const uint16_t *__restrict__ X, int n,
                  float *__restrict__ Y, int row_groups, int vec_store) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_b[kChunksPerIter][kGemmCols * kLdsRowBytes];
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int rg = blockIdx.x % row_groups;          // 4 row units per workgroup
+    const int rg = blockIdx.x % row_groups;          // 4 super-tiles per workgroup
     const int ct = blockIdx.x / row_groups;          // column tile
-    const int unit = rg * kGemmWaves + wave;         // this wave's 64-row unit
+    const int unit = rg * kGemmWaves + wave;         // this wave's super-tile
     const int n0 = ct * kGemmCols;
     const int rho = lane & 15, sig = lane >> 4;
-    const int q = rho & 7;
 
-    // This lane's entry tiles: tile pair tp covers tiles unit*4 + 2tp, +1.
-    int tl[2];
+    floatx4_t acc[kSuperTiles][kGemmColSub];
 #pragma unroll
-    for (int tp = 0; tp < 2; ++tp) tl[tp] = unit * kGemmUnitTiles + 2 * tp + (rho >> 3);
-
-    floatx4_t acc[2][2][kGemmColSub];
+    for (int tt = 0; tt < kSuperTiles; ++tt)
 #pragma unroll
-    for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int c = 0; c < kGemmColSub; ++c) acc[tp][h][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < kGemmColSub; ++c) acc[tt][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     auto load_a = [&](AFrag &a, int c) {
-        const int j = c >> 3, grp = c & 7;
+        if (unit < supertiles && c < octets) {
+            const int64_t region = int64_t(unit) * octets + c;
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
+            for (int tt = 0; tt < kSuperTiles; ++tt) a.code[tt] = wq[(region * kSuperTiles + tt) * kLanes + lane];
+            a.scale = ws[region * kLanes + lane];
+        } else {
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                const int i = 4 * f + sig;
-                if (tl[tp] < tiles) {
-                    const int64_t entry = int64_t(tl[tp]) * steps + j;
-                    a.code[tp][f] = wq[entry * (kRowPairs * kLanes) + grp * 64 + q * 8 + i];
-                    a.scale[tp][f] = *reinterpret_cast<const uint16_t *>(
-                        ws + (entry * kLanes + grp * 8 + i) * 16 + 2 * q);
-                } else {
-                    a.code[tp][f] = make_uint4(0u, 0u, 0u, 0u);
-                    a.scale[tp][f] = 0u;
-                }
-            }
+            for (int tt = 0; tt < kSuperTiles; ++tt) a.code[tt] = make_uint4(0u, 0u, 0u, 0u);
+            a.scale = make_uint2(0u, 0u);
         }
     };
     // X for chunk c (128 k) of this workgroup's columns: 16 bytes per thread
@@ -138,45 +118,38 @@ gemm_mfma_kernel(const uint4 *__restrict__ wq, const uint8_t *__restrict__ ws, f
         }
     };
     auto compute = [&](const AFrag &a, int buf) {
+        // Scale words of row rho of every tile: blocks 0..3 and 4..7 of the octet.
+        uint32_t s0[4], s1[4];
+        gather_lane_groups(a.scale.x, s0);
+        gather_lane_groups(a.scale.y, s1);
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            // Decode: operand (tp, h, e) from dword 2h + e of entry (tp, f).
-            bf16x8_t afr[2][2][2];
+        for (int d = 0; d < 4; ++d) {
+            const int ib = 2 * d + (sig >> 1);   // this lane's block of pair d
+            bf16x8_t afr[kSuperTiles];
 #pragma unroll
-            for (int tp = 0; tp < 2; ++tp) {
-                const uint4 cw = a.code[tp][f];
-                const uint32_t d[4] = {cw.x, cw.y, cw.z, cw.w};
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const float s = e4m3_f32_dyn(a.scale[tp][f], h);
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) afr[tp][h][e] = decode_a(d[2 * h + e], s);
-                }
+            for (int tt = 0; tt < kSuperTiles; ++tt) {
+                const uint32_t sw = d < 2 ? s0[tt] : s1[tt];
+                const float s = e4m3_f32<0>(sw >> (8 * (ib & 3)));
+                const uint4 cw = a.code[tt];
+                afr[tt] = decode_a(d == 0 ? cw.x : d == 1 ? cw.y : d == 2 ? cw.z : cw.w, s);
             }
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
+            for (int cs = 0; cs < kGemmColSub; ++cs) {
+                const int kk = 32 * d + 8 * sig;     // element offset in the chunk
+                const bf16x8_t bfr = *reinterpret_cast<const bf16x8_t *>(
+                    &lds_b[buf][(cs * 16 + rho) * kLdsRowBytes + kk * 2]);
 #pragma unroll
-                for (int cs = 0; cs < kGemmColSub; ++cs) {
-                    const int kk = f * 64 + sig * 16 + e * 8;     // element offset in the chunk
-                    const bf16x8_t bfr = *reinterpret_cast<const bf16x8_t *>(
-                        &lds_b[buf][(cs * 16 + rho) * kLdsRowBytes + kk * 2]);
-#pragma unroll
-                    for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-                        for (int h = 0; h < 2; ++h)
-                            acc[tp][h][cs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[tp][h][e], bfr,
-                                                                                     acc[tp][h][cs], 0, 0, 0);
-                }
+                for (int tt = 0; tt < kSuperTiles; ++tt)
+                    acc[tt][cs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr[tt], bfr, acc[tt][cs], 0, 0, 0);
             }
         }
     };
 
     // An iteration multiplies kChunksPerIter chunks (one LDS buffer each)
     // while the next iteration's weights and activations are in flight in
-    // registers.  `chunks` is a multiple of kChunksPerIter (trailing all-zero
-    // chunks stay inside the padded planes and the activation guard), and the
-    // last iteration re-requests its own chunks instead of branching, so the
-    // loop body is straight-line.
+    // registers.  `chunks` is a multiple of kChunksPerIter (chunks past the
+    // last octet read as zeros), and the last iteration re-requests its own
+    // chunks instead of branching, so the loop body is straight-line.
     AFrag a_cur[kChunksPerIter], a_nxt[kChunksPerIter];
     uint4 b_nxt[kChunksPerIter * kBPasses];
 #pragma unroll
@@ -205,30 +178,22 @@ gemm_mfma_kernel(const uint4 *__restrict__ wq, const uint8_t *__restrict__ ws, f
         __syncthreads();
     }
 
-    // Lane group s holds output slots 4s..4s+3 of every MFMA tile; slot p of
-    // operand h is row 2 (p mod 8) + h of tile 2tp + (p >= 8), so the lane
-    // holds rows 8 (s & 1) .. 8 (s & 1) + 7 of tile unit*4 + 2tp + (s >> 1).
+    // Lane group s holds rows 4s .. 4s + 3 of each tile for column rho of
+    // every column subtile.
 #pragma unroll
-    for (int tp = 0; tp < 2; ++tp) {
-        const int tile = unit * kGemmUnitTiles + 2 * tp + (sig >> 1);
-        const int row0 = tile * kTileRows + (sig & 1) * 8;
+    for (int tt = 0; tt < kSuperTiles; ++tt) {
+        const int row0 = unit * kSuperRows + tt * kTileRows + 4 * sig;
 #pragma unroll
         for (int cs = 0; cs < kGemmColSub; ++cs) {
             const int col = n0 + cs * 16 + rho;
             if (col >= n || row0 >= rows) continue;
-            float v[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = acc[tp][0][cs][i] * tscale;
-                v[2 * i + 1] = acc[tp][1][cs][i] * tscale;
-            }
             float *dst = Y + int64_t(col) * rows + row0;
-            if (vec_store && row0 + 8 <= rows) {
-                reinterpret_cast<float4 *>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
-                reinterpret_cast<float4 *>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+            const floatx4_t v = acc[tt][cs] * tscale;
+            if (vec_store && row0 + 4 <= rows) {
+                *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
             } else {
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
+                for (int i = 0; i < 4; ++i)
                     if (row0 + i < rows) dst[i] = v[i];
             }
         }
@@ -237,16 +202,15 @@ gemm_mfma_kernel(const uint4 *__restrict__ wq, const uint8_t *__restrict__ ws, f
 
 int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
                 int n, float *Y, hipStream_t stream) {
-    const int64_t units = ceil_div(g.tiles, kGemmUnitTiles);
-    const int64_t row_groups = ceil_div(units, kGemmWaves);
+    const int64_t row_groups = ceil_div(g.supertiles, kGemmWaves);
     const int64_t col_tiles = ceil_div(n, kGemmCols);
-    // Chunks of one 8-block group, rounded up to whole iterations; the
-    // planes' 64-block steps always cover them.
-    const int64_t chunks = kChunksPerIter * ceil_div(g.kb, kChunkBlocks * kChunksPerIter);
+    // Octet chunks rounded up to whole iterations; chunks past the last octet
+    // read as zeros.
+    const int64_t chunks = kChunksPerIter * ceil_div(g.octets, kChunksPerIter);
     hipLaunchKernelGGL(gemm_mfma_kernel, dim3(unsigned(row_groups * col_tiles)), dim3(kGemmWaves * kLanes), 0,
-                       stream, reinterpret_cast<const uint4 *>(wq), ws, tscale, int(g.rows), int(g.tiles),
-                       int(g.steps), int(chunks), int(g.cols), X, n, Y, int(row_groups),
-                       int(aligned(Y, 16) && g.rows % 4 == 0));
+                       stream, reinterpret_cast<const uint4 *>(wq), reinterpret_cast<const uint2 *>(ws), tscale,
+                       int(g.rows), int(g.supertiles), int(g.octets), int(chunks), int(g.cols), X, n, Y,
+                       int(row_groups), int(aligned(Y, 16) && g.rows % 4 == 0));
     return launch_status();
 }
 

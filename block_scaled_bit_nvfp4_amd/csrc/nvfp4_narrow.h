@@ -1,0 +1,219 @@
+// nvfp4_narrow.h -- the matrix-vector product for n <= 8 activation columns
+// (decode and the batched speculative verify), shared by the plain, argmax
+// and fused gate||up+SwiGLU kernels of libnvfp4.  Internal to the library.
+//
+// Each 16-element block's dot product runs on v_mfma_f32_16x16x32_bf16, the
+// block scale and the running sum on the VALU:
+//
+//   B operand (32 k x 16 rows): lane l = 16g + r of a code entry holds 8 codes
+//     of row r, elements 32p + 8g .. +7 of block pair p -- exactly one 32-bit
+//     word of the repacked entry, decoded by four v_cvt_scalef32_pk_bf16_fp4
+//     (exact).  Lane groups 0,1 carry the pair's even block, groups 2,3 its
+//     odd block.
+//   A operand (16 slots x 32 k): slot s holds activation column
+//     c(s) = (s >> 2) + 4 ((s >> 1) & 1) restricted to block parity s & 1:
+//     x values where the lane group's block has that parity, zeros elsewhere.
+//   D (16 slots x 16 rows): lane (g, r) receives slots 4g .. 4g + 3 of row r,
+//     i.e. the even- and odd-block partial sums of columns g and g + 4, each
+//     the exact block dot product rounded by the MFMA's fp32 accumulation.
+//   acc += e4m3(scale) * D, one fp32 FMA per block, in block order.
+//
+// Column c always sits in the same slots and lanes whatever n is, and the
+// MFMA computes each output independently of the other slots, so column c of
+// an n-column product equals the 1-column product bit for bit.  The work
+// decomposition (tiles per workgroup, k split) depends only on the matrix
+// shape, so results are also reproducible run to run.
+//
+// Memory: a workgroup owns `tww` tiles of one 64-row super-tile and splits the
+// row's octets (8 blocks) over `ksplit` waves; each wave streams its octets
+// with range-checked buffer loads, one octet ahead of the MFMAs: per tile one
+// 16-byte code load (the tile's 1 KiB chunk), the scales of its rows, and one
+// compact 16-byte activation load that v_ds_bpermute_b32 spreads into the A
+// operand.  Loads past the wave's last octet read zeros with no memory
+// traffic, so the loop needs no branch around a load.
+#pragma once
+
+#include "nvfp4_host.h"
+
+namespace nvfp4 {
+
+constexpr int kMaxNarrowN = 8;
+constexpr int kMaxKsplit = 16;
+// Longest rows the narrow products take: a super-tile's code regions and the
+// activations of 8 columns stay below 2^31 bytes of buffer offset.
+constexpr int64_t kMaxNarrowCols = int64_t(1) << 26;
+
+// Decomposition of a rows x cols product over workgroups; a function of the
+// shape only.  Very tall matrices take whole super-tiles per workgroup (the
+// activation and scale loads are shared by four tiles), mid-size ones two
+// tiles, small ones one tile so that every CU gets work.  The k split aims at
+// about 8192 waves in all.
+struct NarrowConfig {
+    int tww;      // tiles per workgroup: 1, 2 or 4
+    int ksplit;   // waves per workgroup (octet ranges)
+    int64_t groups;   // workgroups
+};
+
+inline NarrowConfig narrow_config(const Geometry &g) {
+    NarrowConfig c;
+    c.tww = g.tiles >= 8192 ? 4 : (g.tiles * g.octets >= 32768 ? 2 : 1);
+    c.groups = g.supertiles * (kSuperTiles / c.tww);
+    int64_t k = ceil_div(8192, c.groups);
+    if (k > kMaxKsplit) k = kMaxKsplit;
+    if (k > g.octets) k = g.octets;
+    if (k < 1) k = 1;
+    c.ksplit = int(k);
+    return c;
+}
+
+// Argmax key: order-preserving map of an fp32 value (with -0 folded into +0)
+// in the high word, the complement of the row index in the low word, so the
+// unsigned maximum picks the largest value and, among equals, the lowest row.
+__device__ __forceinline__ unsigned long long argmax_key(float y, uint32_t row) {
+    uint32_t b = __float_as_uint(y == 0.0f ? 0.0f : y);
+    uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return (static_cast<unsigned long long>(k) << 32) | (0xFFFFFFFFu - row);
+}
+
+template <int TWW>
+constexpr int scale_loads() { return TWW == 4 ? 1 : TWW; }
+
+// One octet of one wave's operands.
+template <int NC, int TWW>
+struct OctetData {
+    u32x4 code[TWW];                 // lane's 16-byte code entry of each tile
+    u32x2 scale[scale_loads<TWW>()]; // TWW == 4: lane 16tt + r holds tile tt row r; else row r of each tile
+    u32x4 x[NC];                     // compact activations: lane 16c + 4p + q holds X[c][128o + 32p + 8q ..]
+};
+
+// acc[tt][h]: this wave's share (octets [o0, o1)) of rows 16 (tile) + r of
+// tile tg * TWW + tt of super-tile st, for columns g + 4h (lane = 16g + r).
+template <int N, int TWW>
+__device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws,
+                                                  int64_t st, int tg, int o0, int o1, int octets, int kb,
+                                                  const uint16_t *__restrict__ X, int K, int lane,
+                                                  float (&acc)[TWW][N > 4 ? 2 : 1]) {
+    constexpr int NC = N > 4 ? 2 : 1;
+    constexpr int H = NC;
+    const int g = lane >> 4, r = lane & 15;
+
+    const auto crs = make_rsrc(wq + st * octets * int64_t(kCodeRegion), uint32_t(o1) * kCodeRegion);
+    const auto srs = make_rsrc(ws + st * octets * int64_t(kScaleRegion), uint32_t(o1) * kScaleRegion);
+    const auto xrs = make_rsrc(X, uint32_t(N) * uint32_t(K) * 2u);
+    const uint32_t coff = uint32_t(lane * 16 + tg * TWW * kCodeChunk);
+    const uint32_t soff = TWW == 4 ? uint32_t(lane * 8) : uint32_t((tg * TWW * kTileRows + r) * 8);
+
+    // Compact activation load of this lane: column xc (+4), k = 128o + 32xp + 8xq.
+    const int xc = lane >> 4, xp = (lane >> 2) & 3, xq = lane & 3;
+    const int xblk = 2 * xp + (xq >> 1);   // its block within the octet
+    uint32_t xvo[NC];
+#pragma unroll
+    for (int h = 0; h < NC; ++h) {
+        const int c = xc + 4 * h;
+        xvo[h] = c < N ? uint32_t((c * K + 32 * xp + 8 * xq) * 2) : kOutOfRange;
+    }
+    // A-operand role of this lane: slot r of k-group g.
+    const int cs = (r >> 2) + 4 * ((r >> 1) & 1);
+    const bool active = cs < N && (g >> 1) == (r & 1);
+    const int src = 4 * (16 * (cs & 3) + g);   // + 16p: byte address of the compact lane
+
+    float part[TWW][H][2];
+#pragma unroll
+    for (int tt = 0; tt < TWW; ++tt)
+#pragma unroll
+        for (int h = 0; h < H; ++h) part[tt][h][0] = part[tt][h][1] = 0.0f;
+
+    auto load = [&](OctetData<NC, TWW> &d, int o) {
+        const uint32_t co = uint32_t(o) * kCodeRegion + coff, so = uint32_t(o) * kScaleRegion + soff;
+#pragma unroll
+        for (int tt = 0; tt < TWW; ++tt)
+            d.code[tt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, co + tt * kCodeChunk, 0, kStream));
+#pragma unroll
+        for (int tt = 0; tt < scale_loads<TWW>(); ++tt)
+            d.scale[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(srs, so + tt * kScaleChunk, 0, kStream));
+#pragma unroll
+        for (int h = 0; h < NC; ++h) {
+            const uint32_t vo = (o * kOctet + xblk < kb) ? xvo[h] : kOutOfRange;   // ragged last octet
+            d.x[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, vo, uint32_t(o) * 256u, 0));
+        }
+    };
+
+    auto compute = [&](const OctetData<NC, TWW> &d) {
+        uint32_t S[2][TWW];   // scale words (blocks 0..3, 4..7 of the octet) of each tile's row r
+        if (TWW == 4) {
+            uint32_t t0[4], t1[4];
+            gather_lane_groups(d.scale[0][0], t0);
+            gather_lane_groups(d.scale[0][1], t1);
+#pragma unroll
+            for (int tt = 0; tt < TWW; ++tt) {
+                S[0][tt] = t0[tt];
+                S[1][tt] = t1[tt];
+            }
+        } else {
+#pragma unroll
+            for (int tt = 0; tt < TWW; ++tt) {
+                S[0][tt] = d.scale[tt][0];
+                S[1][tt] = d.scale[tt][1];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            u32x4 av;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t v = __builtin_amdgcn_ds_bpermute(src + 16 * p, d.x[0][j]);
+                if (NC == 2) {
+                    const uint32_t v2 = __builtin_amdgcn_ds_bpermute(src + 16 * p, d.x[NC - 1][j]);
+                    v = (cs >> 2) ? v2 : v;
+                }
+                av[j] = active ? v : 0u;
+            }
+            const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+#pragma unroll
+            for (int tt = 0; tt < TWW; ++tt) {
+                const floatx4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, e2m1x8_bf16(d.code[tt][p]),
+                                                                        floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                const uint32_t sw = S[p >> 1][tt];
+                const float se = (p & 1) ? e4m3_f32<2>(sw) : e4m3_f32<0>(sw);   // block 2p of the octet
+                const float so = (p & 1) ? e4m3_f32<3>(sw) : e4m3_f32<1>(sw);   // block 2p + 1
+                float &a0 = part[tt][0][p & 1];
+                a0 = __builtin_fmaf(se, D[0], a0);
+                a0 = __builtin_fmaf(so, D[1], a0);
+                if (H == 2) {
+                    float &a1 = part[tt][H - 1][p & 1];
+                    a1 = __builtin_fmaf(se, D[2], a1);
+                    a1 = __builtin_fmaf(so, D[3], a1);
+                }
+            }
+        }
+    };
+
+    // Two octets in flight: full iterations prefetch unconditionally (always
+    // inside [o0, o1)); the tail covers the last one to three octets.
+    OctetData<NC, TWW> buf[2];
+    if (o0 < o1) {
+        const int n = o1 - o0;
+        load(buf[0], o0);
+        const int full = (n - 1) / 2;   // iterations whose two prefetches stay in range
+        int o = o0;
+        for (int it = 0; it < full; ++it, o += 2) {
+            load(buf[1], o + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(buf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            load(buf[0], o + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(buf[1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (o + 1 < o1) load(buf[1], o + 1);
+        compute(buf[0]);
+        if (o + 1 < o1) compute(buf[1]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < TWW; ++tt)
+#pragma unroll
+        for (int h = 0; h < H; ++h) acc[tt][h] = part[tt][h][0] + part[tt][h][1];
+}
+
+}  // namespace nvfp4

@@ -3,7 +3,7 @@
 //
 // quantise: fp32 -> canonical NVFP4, the at-load re-encode of higher
 //   precision weights (bw24 wiki, feature list, safetensors-loader item).
-// repack:   canonical -> split-plane tiles read by the products (bw24 wiki,
+// repack:   canonical -> split-plane regions read by the products (bw24 wiki,
 //   feature list, NVFP4 decode-path item; the loader's NVFP4 repack is
 //   byte-exact, and so is this one).
 // dequant:  repacked -> fp32 / bf16, a verification export of the decode.
@@ -78,104 +78,92 @@ __global__ void __launch_bounds__(256) quantize_kernel(const float4 *__restrict_
 
 // ------------------------------------------------------------------- repack
 
-// Threads [0, code_units) write one 16-byte code entry each; threads
-// [code_units, code_units + scale_units) one 16-byte scale entry each.
+// Threads [0, code_units) write one 16-byte code entry (st, o, tt, lane)
+// each; threads [code_units, code_units + scale_units) one 8-byte scale entry
+// (st, o, tt, r) each.
 __global__ void __launch_bounds__(256) repack_kernel(const uint8_t *__restrict__ codes,
-                                                     const uint8_t *__restrict__ scales,
-                                                     int64_t rows, int64_t cols, int64_t steps,
-                                                     int64_t code_units, int64_t scale_units,
-                                                     uint4 *__restrict__ wq, uint4 *__restrict__ ws) {
+                                                     const uint8_t *__restrict__ scales, int64_t rows,
+                                                     int64_t cols, int64_t octets, int64_t code_units,
+                                                     int64_t scale_units, uint4 *__restrict__ wq,
+                                                     uint2 *__restrict__ ws) {
     int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const int64_t kb = cols / kBlock;
     if (u < code_units) {
-        // u = (((t * steps + j) * 8 + g) * 8 + q) * 8 + i, block 64j + 8g + i
-        const int64_t i = u % 8, q = (u / 8) % kRowPairs, grp = (u / 64) % 8, rest = u / 512;
-        const int64_t j = rest % steps, t = rest / steps;
-        const int64_t b = j * kLanes + grp * 8 + i;
-        int64_t r0 = t * kTileRows + 2 * q;
-        uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
-        if (b < kb) {
-            if (r0 < rows) lo = *reinterpret_cast<const uint2 *>(codes + r0 * (cols / 2) + b * 8);
-            if (r0 + 1 < rows) hi = *reinterpret_cast<const uint2 *>(codes + (r0 + 1) * (cols / 2) + b * 8);
+        const int l = int(u % kLanes), tt = int((u / kLanes) % kSuperTiles);
+        const int64_t rest = u / (kLanes * kSuperTiles), o = rest % octets, st = rest / octets;
+        const int g = l >> 4, r = l & 15;
+        const int64_t row = st * kSuperRows + tt * kTileRows + r;
+        uint32_t v[4] = {0u, 0u, 0u, 0u};
+        if (row < rows) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const int64_t b = o * kOctet + 2 * d + (g >> 1);
+                if (b < kb) v[d] = *reinterpret_cast<const uint32_t *>(codes + row * (cols / 2) + b * 8 + 4 * (g & 1));
+            }
         }
-        wq[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        wq[u] = make_uint4(v[0], v[1], v[2], v[3]);
         return;
     }
     u -= code_units;
     if (u >= scale_units) return;
-    // u = (t * steps + j) * 64 + l
-    int64_t l = u % kLanes, rest = u / kLanes;
-    int64_t j = rest % steps, t = rest / steps;
-    int64_t b = j * kLanes + l;
-    uint32_t v[4] = {0u, 0u, 0u, 0u};
-    if (b < kb) {
+    const int r = int(u % kTileRows), tt = int((u / kTileRows) % kSuperTiles);
+    const int64_t rest = u / (kTileRows * kSuperTiles), o = rest % octets, st = rest / octets;
+    const int64_t row = st * kSuperRows + tt * kTileRows + r;
+    uint32_t v[2] = {0u, 0u};
+    if (row < rows) {
 #pragma unroll
-        for (int i = 0; i < kTileRows; ++i) {
-            int64_t r = t * kTileRows + i;
-            if (r < rows) v[i >> 2] |= uint32_t(scales[r * kb + b]) << (8 * (i & 3));
+        for (int i = 0; i < kOctet; ++i) {
+            const int64_t b = o * kOctet + i;
+            if (b < kb) v[i >> 2] |= uint32_t(scales[row * kb + b]) << (8 * (i & 3));
         }
     }
-    ws[u] = make_uint4(v[0], v[1], v[2], v[3]);
+    ws[u] = make_uint2(v[0], v[1]);
 }
 
 // ------------------------------------------------------------------ dequant
 
-// One thread per 16-byte code entry: 2 rows x 16 elements.
+// One thread per 16-byte code entry: 4 half-blocks (8 elements) of one row.
 __global__ void __launch_bounds__(256) dequant_kernel(const uint4 *__restrict__ wq,
-                                                      const uint4 *__restrict__ ws, float tscale,
-                                                      int64_t rows, int64_t cols, int64_t steps,
+                                                      const uint2 *__restrict__ ws, float tscale,
+                                                      int64_t rows, int64_t cols, int64_t octets,
                                                       int64_t code_units, float *__restrict__ out_f32,
                                                       uint16_t *__restrict__ out_bf16) {
-    int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t u = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     if (u >= code_units) return;
-    const int64_t i = u % 8, q = (u / 8) % kRowPairs, grp = (u / 64) % 8, rest = u / 512;
-    const int64_t j = rest % steps, t = rest / steps;
-    const int64_t l = grp * 8 + i;
-    const int64_t b = j * kLanes + l;
-    if (b >= cols / kBlock) return;
+    const int l = int(u % kLanes), tt = int((u / kLanes) % kSuperTiles);
+    const int64_t rest = u / (kLanes * kSuperTiles), o = rest % octets, st = rest / octets;
+    const int g = l >> 4, r = l & 15;
+    const int64_t row = st * kSuperRows + tt * kTileRows + r;
+    if (row >= rows) return;
     const uint4 c = wq[u];
-    const uint4 sc = ws[(t * steps + j) * kLanes + l];
-    const uint32_t sw[4] = {sc.x, sc.y, sc.z, sc.w};
+    const uint2 sc = ws[(rest * kSuperTiles + tt) * kTileRows + r];
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int64_t r = t * kTileRows + 2 * q + h;
-        if (r >= rows) break;
-        const int ri = 2 * int(q) + h;
-        const float s = e4m3_f32_dyn(sw[ri >> 2], ri & 3);
-        const uint32_t d[2] = {h ? c.z : c.x, h ? c.w : c.y};
-        uint32_t pairs[8];
+    for (int d = 0; d < 4; ++d) {
+        const int ib = 2 * d + (g >> 1);                 // block within the octet
+        const int64_t b = o * kOctet + ib;
+        if (b >= cols / kBlock) continue;
+        const float s = e4m3_f32_dyn(ib < 4 ? sc.x : sc.y, ib & 3);
+        const uint32_t pairs[4] = {as_u32(e2m1x2_bf16<0>(cw[d])), as_u32(e2m1x2_bf16<1>(cw[d])),
+                                   as_u32(e2m1x2_bf16<2>(cw[d])), as_u32(e2m1x2_bf16<3>(cw[d]))};
+        float v[8];
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            pairs[4 * w + 0] = as_u32(e2m1x2_bf16<0>(d[w]));
-            pairs[4 * w + 1] = as_u32(e2m1x2_bf16<1>(d[w]));
-            pairs[4 * w + 2] = as_u32(e2m1x2_bf16<2>(d[w]));
-            pairs[4 * w + 3] = as_u32(e2m1x2_bf16<3>(d[w]));
-        }
-        float v[16];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
+        for (int p = 0; p < 4; ++p) {
             v[2 * p + 0] = __uint_as_float(pairs[p] << 16) * s;          // exact
             v[2 * p + 1] = __uint_as_float(pairs[p] & 0xFFFF0000u) * s;  // exact
         }
-        const int64_t off = r * cols + b * kBlock;
+        const int64_t off = row * cols + b * kBlock + 8 * (g & 1);
         if (out_bf16) {
-            uint4 *dst = reinterpret_cast<uint4 *>(out_bf16 + off);
+            uint32_t w[4];
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                uint32_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[e] = (__float_as_uint(v[8 * p + 2 * e]) >> 16) |
-                           (__float_as_uint(v[8 * p + 2 * e + 1]) & 0xFFFF0000u);
-                dst[p] = make_uint4(o[0], o[1], o[2], o[3]);
-            }
+            for (int e = 0; e < 4; ++e)
+                w[e] = (__float_as_uint(v[2 * e]) >> 16) | (__float_as_uint(v[2 * e + 1]) & 0xFFFF0000u);
+            *reinterpret_cast<uint4 *>(out_bf16 + off) = make_uint4(w[0], w[1], w[2], w[3]);
         }
         if (out_f32) {
             float4 *dst = reinterpret_cast<float4 *>(out_f32 + off);
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                dst[p] = make_float4(v[4 * p] * tscale, v[4 * p + 1] * tscale, v[4 * p + 2] * tscale,
-                                     v[4 * p + 3] * tscale);
+            dst[0] = make_float4(v[0] * tscale, v[1] * tscale, v[2] * tscale, v[3] * tscale);
+            dst[1] = make_float4(v[4] * tscale, v[5] * tscale, v[6] * tscale, v[7] * tscale);
         }
     }
 }
@@ -212,11 +200,11 @@ NVFP4_API int nvfp4_repack(const uint8_t *codes, const uint8_t *scales, int64_t 
     if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(wq, 16) || !aligned(ws, 16))
         return NVFP4_EALIGN;
     const Geometry g(rows, cols);
-    const int64_t code_units = int64_t(g.code_bytes() / 16), scale_units = int64_t(g.scale_bytes() / 16);
+    const int64_t code_units = int64_t(g.code_bytes() / 16), scale_units = int64_t(g.scale_bytes() / 8);
     (void)hipGetLastError();
     hipLaunchKernelGGL(repack_kernel, dim3(unsigned(ceil_div(code_units + scale_units, 256))), dim3(256),
-                       0, stream, codes, scales, rows, cols, g.steps, code_units, scale_units,
-                       reinterpret_cast<uint4 *>(wq), reinterpret_cast<uint4 *>(ws));
+                       0, stream, codes, scales, rows, cols, g.octets, code_units, scale_units,
+                       reinterpret_cast<uint4 *>(wq), reinterpret_cast<uint2 *>(ws));
     return launch_status();
 }
 
@@ -230,7 +218,7 @@ NVFP4_API int nvfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, 
     const int64_t code_units = int64_t(g.code_bytes() / 16);
     (void)hipGetLastError();
     hipLaunchKernelGGL(dequant_kernel, dim3(unsigned(ceil_div(code_units, 256))), dim3(256), 0, stream,
-                       reinterpret_cast<const uint4 *>(wq), reinterpret_cast<const uint4 *>(ws), tscale,
-                       rows, cols, g.steps, code_units, out_f32, out_bf16);
+                       reinterpret_cast<const uint4 *>(wq), reinterpret_cast<const uint2 *>(ws), tscale,
+                       rows, cols, g.octets, code_units, out_f32, out_bf16);
     return launch_status();
 }

@@ -30,20 +30,22 @@
  *   scales uint8 [rows][cols/16]: scale of elements 16b..16b+15 at [r][b].
  *
  * Repacked layout (what the products read; "split-plane": codes and scales
- * are two separate planes).  Let T = ceil(rows/16) row tiles, KB = cols/16
- * blocks per row, S = ceil(KB/64) steps of 64 blocks; a step's blocks form 8
- * groups of 8.
- *   code plane  uint8 [T][S][8][8][8][16]: entry (t, j, g, q, i) holds the 8
- *       canonical code bytes of block b = 64j + 8g + i of row 16t + 2q in
- *       bytes 0..7 and of row 16t + 2q + 1 in bytes 8..15;
- *   scale plane uint8 [T][S][64][16]: byte i of entry (t, j, l) is the scale
- *       of block 64j + l of row 16t + i;
+ * are two separate planes).  Rows are grouped in tiles of 16 and tiles in
+ * super-tiles of 4 (64 rows); the 16-element blocks of a row in octets of 8.
+ * Let T = ceil(rows/16), ST = ceil(T/4), KB = cols/16, O = ceil(KB/8).
+ *   code plane  uint8 [ST][O][4][64][16]: entry (st, o, tt, l), l = 16g + r
+ *       (g = 0..3, r = 0..15), belongs to row 64st + 16tt + r; its bytes
+ *       4d..4d+3 (d = 0..3) are the canonical code bytes of elements
+ *       8h..8h+7 of block 8o + 2d + (g >> 1) of that row, h = g & 1 -- so
+ *       word d of the entry holds elements 32(4o + d) + 8g .. +7 of the row;
+ *   scale plane uint8 [ST][O][4][16][8]: entry (st, o, tt, r) byte i is the
+ *       scale of block 8o + i of row 64st + 16tt + r;
  *   positions past the last row or block hold 0.
- * A 64-lane wavefront of the matvec gives lane l block 64j + l: for row pair
- * q its 64 code entries are 8 full 128-byte lines of the (t, j) region, and
- * its scale entry (t, j) is 1 KiB contiguous -- 128-bit coalesced loads, each
- * byte once per call for all N columns.  The wide contraction reads a group
- * of 8 blocks of a tile as 1 KiB contiguous.
+ * One tile's octet is a 1 KiB code chunk that a 64-lane wavefront reads with
+ * one 128-bit load per lane, and its 16 rows' scales are 128 contiguous
+ * bytes; each 32-bit word of a code entry is directly the weight operand of
+ * one 16x16x32 MFMA (row r, elements 8g..8g+7 of a 32-element k slice), for
+ * the matvec and the wide contraction alike.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are device memory owned by the caller; the library
@@ -86,7 +88,8 @@ extern "C" {
 const char *nvfp4_strerror(int status);
 
 /* Sizes in bytes of the repacked code and scale planes for a rows x cols
- * matrix (rows padded to 16, blocks to 64), or 0 for an invalid shape. */
+ * matrix (rows padded to 64, blocks to 8): ST * O * 4096 and ST * O * 512,
+ * or 0 for an invalid shape. */
 size_t nvfp4_repacked_code_bytes(int64_t rows, int64_t cols);
 size_t nvfp4_repacked_scale_bytes(int64_t rows, int64_t cols);
 
@@ -127,8 +130,10 @@ int nvfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t ro
  * depends only on (rows, cols): results are bitwise reproducible run to run,
  * and for n <= 8 column c equals, bit for bit, the n = 1 product of X[c]
  * (bw24 wiki, exactness note: summation order is part of the contract).
- * n <= 8 runs the VALU matvec; larger n runs a dequant-to-bf16 MFMA tile
- * contraction.  1 <= n <= NVFP4_MAX_N.  X [n][cols] bf16 bits, Y [n][rows]. */
+ * n <= 8 runs the matvec (block dot products on MFMA, block scales and the
+ * running sum in fp32 on the VALU; cols <= 2^26, else NVFP4_ESHAPE); larger
+ * n runs a dequant-to-bf16 MFMA tile contraction.  1 <= n <= NVFP4_MAX_N.
+ * X [n][cols] bf16 bits, Y [n][rows]. */
 int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
                const uint16_t *X, int n, float *Y, hipStream_t stream);
 
@@ -140,9 +145,9 @@ size_t nvfp4_gemv_argmax_workspace_bytes(int n);
  * index of the largest Y[c][r] (-0 and +0 compare equal) -- the vocabulary
  * projection with the greedy token (bw24 wiki: prefill-argmax vs
  * decode-argmax gate; qwentin README, "How it works": dense-argmax descent).
- * One kernel launch: every 16-row tile folds its per-column maxima into the
- * workspace with 64-bit atomic maxima of (order-preserving value key,
- * complemented row), and the last tile to finish writes argmax.
+ * One kernel launch: every workgroup folds its rows' per-column maxima into
+ * the workspace with 64-bit atomic maxima of (order-preserving value key,
+ * complemented row), and the last workgroup to finish writes argmax.
  * logits [n][rows] may be NULL (not stored).  workspace: device memory of at
  * least nvfp4_gemv_argmax_workspace_bytes(n) bytes, 8-byte aligned, that is
  * all-zero before its first use (e.g. one hipMemset after allocation); every
@@ -168,9 +173,11 @@ int nvfp4_swiglu(const float *gu, int64_t F, int n, uint16_t *h, hipStream_t str
  * bit what nvfp4_gemv followed by nvfp4_swiglu give (the pages'
  * persistent-MLP decode GEMV, qwentin README "How it works", also keeps the
  * MLP's intermediate out of memory).  1 <= n <= 8; F a multiple of 16;
- * gu 4-byte and h 2-byte aligned.  One launch whenever n == 1 or F >= 4096 or
- * hidden <= 4096; other shapes run the plain product into gu (then required,
- * else NVFP4_ESHAPE) and the SwiGLU kernel, with the same bits. */
+ * gu 4-byte and h 2-byte aligned.  One launch when F is a multiple of 64 and
+ * the stacked product splits each row over at most 8 waves (true for the
+ * 27B-class MLP, F = 17408, hidden = 5120); other shapes run the plain
+ * product into gu (then required, else NVFP4_ESHAPE) and the SwiGLU kernel,
+ * with the same bits. */
 int nvfp4_gemv_swiglu(const uint8_t *wq_gu, const uint8_t *ws_gu, float tscale, int64_t hidden,
                       int64_t F, const uint16_t *X, int n, float *gu, uint16_t *h, hipStream_t stream);
 

@@ -240,9 +240,9 @@ def repack(codes, scales):
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
     R, K = codes.shape[0], codes.shape[1] * 2
     _check_shape(R, K)
-    T = (R + 15) // 16
-    S = (K // 16 + 63) // 64
-    wq = np.empty(T * S * 8 * 64 * 16, np.uint8)
-    ws = np.empty(T * S * 64 * 16, np.uint8)
+    ST = ((R + 15) // 16 + 3) // 4
+    O = (K // 16 + 7) // 8
+    wq = np.empty(ST * O * 4 * 64 * 16, np.uint8)
+    ws = np.empty(ST * O * 4 * 16 * 8, np.uint8)
     _load().oracle_repack(_ptr(codes), _ptr(scales), R, K, _ptr(wq), _ptr(ws))
     return wq, ws

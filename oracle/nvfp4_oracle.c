@@ -273,14 +273,16 @@ uint16_t oracle_bf16_rne(double v)
 
 /* Reference of the library's repacked ("split-plane") layout, written from
  * its published definition, not from the library's code.  The definition:
- *   rows are grouped in tiles of 16; blocks (16 elements) of a row are
- *   grouped in steps of 64, and a step's blocks in 8 groups of 8;
- *   T = ceil(R/16), KB = K/16, S = ceil(KB/64);
- *   code plane  [T][S][8][8][8][16 bytes]: entry (t, j, g, q, i) holds the 8
- *     canonical code bytes of block b = 64j + 8g + i of row 16t + 2q in
- *     bytes 0..7 and the same block of row 16t + 2q + 1 in bytes 8..15;
- *   scale plane [T][S][64][16 bytes]: entry (t, j, l) byte i is the scale
- *     of block 64j + l of row 16t + i;
+ *   rows are grouped in tiles of 16 and tiles in super-tiles of 4 (64
+ *   rows); the 16-element blocks of a row are grouped in octets of 8;
+ *   T = ceil(R/16), ST = ceil(T/4), KB = K/16, O = ceil(KB/8);
+ *   code plane  [ST][O][4][64][16 bytes]: entry (st, o, tt, l), with
+ *     l = 16g + r (g = 0..3, r = 0..15), belongs to row 64st + 16tt + r; its
+ *     bytes 4d..4d+3 (d = 0..3) are the 4 canonical code bytes holding
+ *     elements 8h..8h+7 of block b = 8o + 2d + (g >> 1) of that row, with
+ *     h = g & 1;
+ *   scale plane [ST][O][4][16][8 bytes]: entry (st, o, tt, r) byte i is the
+ *     scale of block 8o + i of row 64st + 16tt + r;
  *   positions past the last row or block hold 0.
  * The inverse is checked separately. */
 void oracle_repack(const uint8_t *codes, const uint8_t *scales, int64_t R, int64_t K,
@@ -288,26 +290,21 @@ void oracle_repack(const uint8_t *codes, const uint8_t *scales, int64_t R, int64
 {
     int64_t KB = K / 16;
     int64_t T = (R + 15) / 16;
-    int64_t S = (KB + 63) / 64;
-    memset(wq, 0, (size_t)(T * S * 8 * 64 * 16));
-    memset(ws, 0, (size_t)(T * S * 64 * 16));
-    for (int64_t t = 0; t < T; ++t)
-        for (int64_t j = 0; j < S; ++j)
-            for (int64_t l = 0; l < 64; ++l) {
-                int64_t b = 64 * j + l;
-                int64_t g = l / 8, i = l % 8;
-                if (b >= KB) continue;
-                for (int64_t q = 0; q < 8; ++q)
-                    for (int64_t h = 0; h < 2; ++h) {
-                        int64_t r = 16 * t + 2 * q + h;
-                        if (r >= R) continue;
-                        uint8_t *dst = wq + ((((t * S + j) * 8 + g) * 8 + q) * 8 + i) * 16 + 8 * h;
-                        memcpy(dst, codes + r * (K / 2) + 8 * b, 8);
-                    }
-                for (int64_t i16 = 0; i16 < 16; ++i16) {
-                    int64_t r = 16 * t + i16;
-                    if (r >= R) continue;
-                    ws[((t * S + j) * 64 + l) * 16 + i16] = scales[r * KB + b];
-                }
+    int64_t ST = (T + 3) / 4;
+    int64_t O = (KB + 7) / 8;
+    memset(wq, 0, (size_t)(ST * O * 4 * 64 * 16));
+    memset(ws, 0, (size_t)(ST * O * 4 * 16 * 8));
+    for (int64_t row = 0; row < R; ++row) {
+        int64_t st = row / 64, tt = (row % 64) / 16, r = row % 16;
+        for (int64_t b = 0; b < KB; ++b) {
+            int64_t o = b / 8, ib = b % 8;     /* octet, block within the octet */
+            int64_t d = ib / 2, par = ib % 2;  /* block pair, parity within it */
+            for (int64_t h = 0; h < 2; ++h) {
+                int64_t g = 2 * par + h, l = 16 * g + r;
+                uint8_t *dst = wq + (((st * O + o) * 4 + tt) * 64 + l) * 16 + 4 * d;
+                memcpy(dst, codes + row * (K / 2) + 8 * b + 4 * h, 4);
             }
+            ws[(((st * O + o) * 4 + tt) * 16 + r) * 8 + ib] = scales[row * KB + b];
+        }
+    }
 }

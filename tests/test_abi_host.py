@@ -40,8 +40,9 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
     # and nothing from the internal namespace leaks as a C symbol
-    with pytest.raises(AttributeError):
-        getattr(lib, "launch_valu")
+    for internal in ("launch_narrow", "narrow_config", "launch_mfma"):
+        with pytest.raises(AttributeError):
+            getattr(lib, internal)
 
 
 def test_binding_names_match_header():
@@ -50,11 +51,13 @@ def test_binding_names_match_header():
 
 
 @pytest.mark.parametrize("rows,cols,code,scale", [
-    (256, 512, 16 * 1 * 8192, 16 * 1 * 1024),
-    (4096, 4096, 256 * 4 * 8192, 256 * 4 * 1024),
-    (17, 32, 2 * 8192, 2 * 1024),
-    (151936, 5120, 9496 * 5 * 8192, 9496 * 5 * 1024),
-    (5120, 17408, 320 * 17 * 8192, 320 * 17 * 1024),
+    # (64-row super-tiles) x (octets of 8 blocks) x (4096 | 512) bytes
+    (256, 512, 4 * 4 * 4096, 4 * 4 * 512),
+    (4096, 4096, 64 * 32 * 4096, 64 * 32 * 512),
+    (17, 32, 1 * 1 * 4096, 1 * 1 * 512),
+    (151936, 5120, 2374 * 40 * 4096, 2374 * 40 * 512),
+    (5120, 17408, 80 * 136 * 4096, 80 * 136 * 512),
+    (65, 144, 2 * 2 * 4096, 2 * 2 * 512),
 ])
 def test_plane_sizes(lib, rows, cols, code, scale):
     assert nv.nvfp4_repacked_code_bytes(rows, cols) == code
@@ -102,6 +105,8 @@ def test_gemv_validation(lib):
     assert g(A, B, 1.0, 16, 32, MIS, 1, A, S0) == EALIGN
     assert g(A, B, 1.0, 16, 32, C, 1, ctypes.c_void_p(0x100002), S0) == EALIGN
     assert g(A, B, 1.0, 16, 32, C, 1, NULL, S0) == EINVAL
+    # the n <= 8 products take rows of at most 2^26 elements; wider n does not
+    assert g(A, B, 1.0, 16, (1 << 26) + 16, C, 8, A, S0) == ESHAPE
 
 
 def test_argmax_validation(lib):

@@ -33,8 +33,14 @@ def _bits(t):
     return t.contiguous().view(torch.int32 if t.element_size() == 4 else torch.int16)
 
 
+# Shapes whose stacked product splits k over more than 8 waves per workgroup,
+# which the one-launch kernel cannot hold twice.
+NOT_FUSED = {(4096, 1024), (8192, 1024)}
+
+
 @pytest.mark.parametrize("D,F,n", [(512, 1024, 1), (1040, 2064, 2), (96, 48, 3), (5120, 17408, 1),
-                                   (5120, 17408, 4), (4096, 1024, 8), (8192, 1024, 1), (8192, 1024, 2)])
+                                   (5120, 17408, 4), (4096, 1024, 8), (8192, 1024, 1), (8192, 1024, 2),
+                                   (1008, 1024, 5)])
 def test_gemv_swiglu_equals_two_launches(D, F, n):
     import block_scaled_bit_nvfp4_amd as nv
     _, q, ss = _stacked(D, F, seed=D + F)
@@ -49,12 +55,14 @@ def test_gemv_swiglu_equals_two_launches(D, F, n):
     assert torch.equal(_bits(gu), _bits(gu_r))
     assert torch.equal(_bits(h), _bits(h_r))
     h2 = torch.zeros(n, F, dtype=torch.bfloat16, device=G.DEV)       # without the gu output
-    if n == 1 or F >= 4096 or D <= 4096:
+    try:
         nv.nvfp4_gemv_swiglu(q, ss, 0.75, D, F, X, n, None, h2)
-        assert torch.equal(_bits(h2), _bits(h_r))
-    else:
-        with pytest.raises(nv.NVFP4Error):
-            nv.nvfp4_gemv_swiglu(q, ss, 0.75, D, F, X, n, None, h2)
+    except nv.NVFP4Error as err:
+        # only shapes the one-launch kernel cannot take may refuse a missing gu
+        assert err.status == -2 and (F % 64 != 0 or (D, F) in NOT_FUSED), (D, F)
+        return
+    assert F % 64 == 0
+    assert torch.equal(_bits(h2), _bits(h_r))
 
 
 def test_mlp_layer_vs_oracle_at_27b_shape():

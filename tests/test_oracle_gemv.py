@@ -174,21 +174,23 @@ def test_bf16_rne_array():
 def _unrepack(wq, ws, R, K):
     """Inverse of the repacked layout, written from its definition."""
     KB, T = K // 16, (R + 15) // 16
-    S = (KB + 63) // 64
+    ST, O = (T + 3) // 4, (KB + 7) // 8
     codes = np.zeros((R, K // 2), np.uint8)
     scales = np.zeros((R, KB), np.uint8)
-    cq = wq.reshape(T, S, 8, 8, 8, 2, 8)      # [t][j][g][q][i][row of pair][byte]
-    sq = ws.reshape(T, S, 64, 16)
-    for r in range(R):
-        t, q, h = r // 16, (r % 16) // 2, r % 2
+    cq = wq.reshape(ST, O, 4, 4, 16, 4, 4)    # [st][o][tile][g][r][dword d][byte]
+    sq = ws.reshape(ST, O, 4, 16, 8)          # [st][o][tile][r][block in octet]
+    for row in range(R):
+        st, tt, r = row // 64, (row % 64) // 16, row % 16
         for b in range(KB):
-            j, g, i = b // 64, (b % 64) // 8, b % 8
-            codes[r, 8 * b:8 * b + 8] = cq[t, j, g, q, i, h]
-            scales[r, b] = sq[t, j, b % 64, r % 16]
+            o, ib = b // 8, b % 8
+            for h in range(2):                # element half of the block
+                g = 2 * (ib % 2) + h
+                codes[row, 8 * b + 4 * h:8 * b + 4 * h + 4] = cq[st, o, tt, g, r, ib // 2]
+            scales[row, b] = sq[st, o, tt, r, ib]
     return codes, scales
 
 
-@pytest.mark.parametrize("R,K", [(17, 32), (16, 1024), (33, 1040), (1, 16), (50, 2064)])
+@pytest.mark.parametrize("R,K", [(17, 32), (16, 1024), (33, 1040), (1, 16), (50, 2064), (130, 272)])
 def test_repack_roundtrip_and_padding(R, K):
     rng = np.random.default_rng(R + K)
     codes = rng.integers(1, 256, (R, K // 2), dtype=np.uint8)
@@ -223,4 +225,4 @@ def test_repack_hand_derived_positions():
             want = scales[int(f[3]), int(f[4])]
         assert plane[off] == want, line
         n += 1
-    assert n == 20
+    assert n == 24
