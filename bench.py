@@ -109,7 +109,8 @@ class Step:
             self.y1 = torch.empty(4, mw.rows, dtype=torch.float32, device=DEV)
             self.logits = torch.empty(4, head.rows, dtype=torch.float32, device=DEV)
             self.am = torch.empty(4, dtype=torch.int32, device=DEV)
-            self.wsp = torch.zeros(nv.nvfp4_gemv_argmax_workspace_bytes(4), dtype=torch.uint8, device=DEV)
+            self.wsp = torch.empty(nv.nvfp4_gemv_argmax_workspace_bytes(head.rows, head.cols, 4), dtype=torch.uint8,
+                                   device=DEV)
             self.launches.append((self._gemv(self.M1, self.x, 4, self.y1), gemv_bytes(mw.rows, mw.cols, 4),
                                   8 * mw.rows * mw.cols, "gemv"))
             self.launches.append((self._argmax(), gemv_bytes(head.rows, head.cols, 4) + 4 * 4,

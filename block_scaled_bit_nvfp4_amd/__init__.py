@@ -62,7 +62,7 @@ def load():
             "nvfp4_repack": (i32, [P, P, i64, i64, P, P, P]),
             "nvfp4_dequant": (i32, [P, P, f32, i64, i64, P, P, P]),
             "nvfp4_gemv": (i32, [P, P, f32, i64, i64, P, i32, P, P]),
-            "nvfp4_gemv_argmax_workspace_bytes": (sz, [i32]),
+            "nvfp4_gemv_argmax_workspace_bytes": (sz, [i64, i64, i32]),
             "nvfp4_gemv_argmax": (i32, [P, P, f32, i64, i64, P, i32, P, P, P, sz, P]),
             "nvfp4_swiglu": (i32, [P, i64, i32, P, P]),
             "nvfp4_gemv_swiglu": (i32, [P, P, f32, i64, i64, P, i32, P, P, P]),
@@ -111,8 +111,8 @@ def nvfp4_repacked_scale_bytes(rows: int, cols: int) -> int:
     return int(load().nvfp4_repacked_scale_bytes(rows, cols))
 
 
-def nvfp4_gemv_argmax_workspace_bytes(n: int) -> int:
-    return int(load().nvfp4_gemv_argmax_workspace_bytes(n))
+def nvfp4_gemv_argmax_workspace_bytes(rows: int, cols: int, n: int) -> int:
+    return int(load().nvfp4_gemv_argmax_workspace_bytes(rows, cols, n))
 
 
 def nvfp4_quantize(W, rows, cols, tscale, codes, scales, stream=None):

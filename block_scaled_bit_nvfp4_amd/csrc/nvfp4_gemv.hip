@@ -42,9 +42,9 @@ __global__ void __launch_bounds__(256) swiglu_kernel(const float *__restrict__ g
 // ------------------------------------------------------------ the products
 
 // MODE kPlain:  Y[c][row] = tscale * sum.
-// MODE kArgmax: as kPlain (Y may be NULL) plus the per-column argmax folded
-//   into amax_ws by 64-bit atomic maxima, one per column and workgroup; the
-//   last workgroup to finish writes argmax_out and clears the workspace.
+// MODE kArgmax: as kPlain (Y may be NULL) plus, per column, the largest
+//   argmax key of the workgroup's rows stored to amax_ws[blockIdx][c];
+//   argmax_finish_kernel, launched next on the stream, reduces them.
 // MODE kSwiglu: the workgroup's waves [0, ksplit) take gate rows, waves
 //   [ksplit, 2 ksplit) the up rows up_st super-tiles further down (the same
 //   positions of the stacked matrix); h[c][row] = bf16(SiLU(g) u) with
@@ -122,34 +122,45 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
                 const unsigned long long other = __shfl_xor(key, o);
                 key = other > key ? other : key;
             }
-            if (lr == 0 && key != 0ull)
-                __hip_atomic_fetch_max(amax_ws + c, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lr == 0) amax_ws[int64_t(blockIdx.x) * N + c] = key;
         }
     }
-    if (MODE == kArgmax) {
-        // The last workgroup to finish turns the keys into row indices and
-        // returns the workspace to all-zero for the next call.  The maxima are
-        // order-independent, so the result does not depend on which one is
-        // last.  Keys and counter are touched only by device-scope atomics,
-        // coherent across the XCDs' L2s without cache maintenance; every
-        // thread waits for its key atomics to complete before the barrier that
-        // precedes the counter increment (an agent-scope fence would write
-        // back and invalidate L2 in every workgroup instead).
-        __shared__ unsigned int last;
-        unsigned int *counter = reinterpret_cast<unsigned int *>(amax_ws + kMaxNarrowN);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (threadIdx.x == 0)
-            last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
-        __syncthreads();
-        if (last) {
-            if (threadIdx.x < N) {
-                const unsigned long long k =
-                    __hip_atomic_exchange(amax_ws + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                argmax_out[threadIdx.x] = int32_t(0xFFFFFFFFu - uint32_t(k));
-            }
-            if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Second launch of the argmax: the product's per-workgroup keys are complete
+// (kernel boundary); the largest key of each column names its row.  The
+// maximum is order-independent, so the result is exact and reproducible.
+constexpr int kFinishThreads = 256;
+
+template <int N>
+__global__ void __launch_bounds__(kFinishThreads)
+argmax_finish_kernel(const unsigned long long *__restrict__ keys, int groups, int32_t *__restrict__ argmax_out) {
+    __shared__ unsigned long long part[kFinishThreads / kLanes][N];
+    unsigned long long m[N];
+#pragma unroll
+    for (int c = 0; c < N; ++c) m[c] = 0ull;
+    for (int g = threadIdx.x; g < groups; g += kFinishThreads)
+#pragma unroll
+        for (int c = 0; c < N; ++c) {
+            const unsigned long long k = keys[int64_t(g) * N + c];
+            m[c] = k > m[c] ? k : m[c];
         }
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+#pragma unroll
+        for (int o = kLanes / 2; o >= 1; o >>= 1) {
+            const unsigned long long other = __shfl_xor(m[c], o);
+            m[c] = other > m[c] ? other : m[c];
+        }
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][c] = m[c];
+    }
+    __syncthreads();
+    if (threadIdx.x < N) {
+        const int c = threadIdx.x;
+        unsigned long long best = part[0][c];
+#pragma unroll
+        for (int w = 1; w < kFinishThreads / kLanes; ++w) best = part[w][c] > best ? part[w][c] : best;
+        argmax_out[c] = int32_t(0xFFFFFFFFu - uint32_t(best));
     }
 }
 
@@ -254,9 +265,10 @@ NVFP4_API int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int
     return launch_mfma(g, wq, ws, tscale, X, n, Y, stream);
 }
 
-NVFP4_API size_t nvfp4_gemv_argmax_workspace_bytes(int n) {
-    // kMaxNarrowN 64-bit keys and a 32-bit completion counter, whatever n.
-    return (n >= 1 && n <= kMaxNarrowN) ? size_t(8) * (kMaxNarrowN + 1) : 0;
+NVFP4_API size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, int n) {
+    // One 64-bit key per workgroup and column.
+    if (n < 1 || n > kMaxNarrowN || check_shape(rows, cols) != NVFP4_OK || cols > kMaxNarrowCols) return 0;
+    return size_t(narrow_config(Geometry(rows, cols)).groups) * size_t(n) * sizeof(unsigned long long);
 }
 
 NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
@@ -266,12 +278,26 @@ NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tsca
     if (int st = check_product_args(wq, ws, tscale, rows, cols, X, n)) return st;
     if (n > kMaxNarrowN) return NVFP4_EINVAL;
     if (!aligned(logits, 4) || !aligned(argmax, 4) || !aligned(workspace, 8)) return NVFP4_EALIGN;
-    if (workspace_bytes < nvfp4_gemv_argmax_workspace_bytes(n)) return NVFP4_EWORKSPACE;
-    if (rows > int64_t(0x7FFFFFFF)) return NVFP4_ESHAPE;
+    if (workspace_bytes < nvfp4_gemv_argmax_workspace_bytes(rows, cols, n)) return NVFP4_EWORKSPACE;
     const Geometry g(rows, cols);
     (void)hipGetLastError();
-    return launch_narrow<kArgmax>(g, wq, ws, tscale, X, n, logits, static_cast<unsigned long long *>(workspace),
-                                  argmax, stream);
+    auto *keys = static_cast<unsigned long long *>(workspace);
+    if (int st = launch_narrow<kArgmax>(g, wq, ws, tscale, X, n, logits, keys, argmax, stream)) return st;
+    const int groups = int(narrow_config(g).groups);
+#define NVFP4_FINISH(NN) \
+    hipLaunchKernelGGL(argmax_finish_kernel<NN>, dim3(1), dim3(kFinishThreads), 0, stream, keys, groups, argmax)
+    switch (n) {
+        case 1: NVFP4_FINISH(1); break;
+        case 2: NVFP4_FINISH(2); break;
+        case 3: NVFP4_FINISH(3); break;
+        case 4: NVFP4_FINISH(4); break;
+        case 5: NVFP4_FINISH(5); break;
+        case 6: NVFP4_FINISH(6); break;
+        case 7: NVFP4_FINISH(7); break;
+        default: NVFP4_FINISH(8); break;
+    }
+#undef NVFP4_FINISH
+    return launch_status();
 }
 
 NVFP4_API int nvfp4_gemv_swiglu(const uint8_t *wq_gu, const uint8_t *ws_gu, float tscale, int64_t hidden,

@@ -137,22 +137,23 @@ int nvfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t ro
 int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
                const uint16_t *X, int n, float *Y, hipStream_t stream);
 
-/* Workspace bytes nvfp4_gemv_argmax needs (72: eight 64-bit keys and a
- * completion counter), 0 if n is out of range. */
-size_t nvfp4_gemv_argmax_workspace_bytes(int n);
+/* Workspace bytes nvfp4_gemv_argmax needs for a rows x cols matrix and n
+ * columns: one 64-bit key per workgroup of the product and column (at most
+ * 4 * rows bytes); 0 for an invalid shape or n out of 1..8. */
+size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, int n);
 
 /* nvfp4_gemv for 1 <= n <= 8 plus, per column c, argmax[c] = the lowest row
  * index of the largest Y[c][r] (-0 and +0 compare equal) -- the vocabulary
  * projection with the greedy token (bw24 wiki: prefill-argmax vs
  * decode-argmax gate; qwentin README, "How it works": dense-argmax descent).
- * One kernel launch: every workgroup folds its rows' per-column maxima into
- * the workspace with 64-bit atomic maxima of (order-preserving value key,
- * complemented row), and the last workgroup to finish writes argmax.
+ * Two launches: the product, whose workgroups each store, per column, the
+ * largest (order-preserving value key, complemented row) of their rows to the
+ * workspace, then a one-workgroup kernel that reduces those keys to row
+ * indices.  No atomics: the result is exact and the same on every run.
  * logits [n][rows] may be NULL (not stored).  workspace: device memory of at
- * least nvfp4_gemv_argmax_workspace_bytes(n) bytes, 8-byte aligned, that is
- * all-zero before its first use (e.g. one hipMemset after allocation); every
- * call leaves it all-zero again.  Calls sharing a workspace must not run
- * concurrently. */
+ * least nvfp4_gemv_argmax_workspace_bytes(rows, cols, n) bytes, 8-byte
+ * aligned, any contents; the call overwrites it.  Calls sharing a workspace
+ * must not run concurrently. */
 int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
                       int64_t cols, const uint16_t *X, int n, float *logits, int32_t *argmax,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);

@@ -60,8 +60,10 @@ def gemv_argmax_gpu(wq, ws, tscale, R, K, X: torch.Tensor, with_logits=True, wor
     n = X.shape[0]
     logits = torch.full((n, R), float("nan"), dtype=torch.float32, device=DEV) if with_logits else None
     am = torch.full((n,), -7, dtype=torch.int32, device=DEV)
-    wsp = workspace if workspace is not None else torch.zeros(
-        nv.nvfp4_gemv_argmax_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    if workspace is None:      # any contents: the call overwrites the workspace
+        workspace = torch.full((nv.nvfp4_gemv_argmax_workspace_bytes(R, K, n),), 0xA5, dtype=torch.uint8,
+                               device=DEV)
+    wsp = workspace
     nv.nvfp4_gemv_argmax(wq, ws, tscale, R, K, X, n, logits, am, wsp)
     return logits, am
 

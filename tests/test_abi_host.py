@@ -71,7 +71,13 @@ def test_plane_sizes_invalid(lib, rows, cols):
 
 
 def test_workspace_bytes(lib):
-    assert [nv.nvfp4_gemv_argmax_workspace_bytes(n) for n in (0, 1, 4, 8, 9)] == [0, 72, 72, 72, 0]
+    # one 64-bit key per workgroup and column: a 16 x 32 matrix runs 4
+    # one-tile workgroups (its 64-row super-tile), the 151936 x 5120 vocabulary
+    # projection 2374 four-tile workgroups
+    assert [nv.nvfp4_gemv_argmax_workspace_bytes(16, 32, n) for n in (0, 1, 4, 8, 9)] == [0, 32, 128, 256, 0]
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 4) == 2374 * 4 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(16, 24, 4) == 0
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(16, (1 << 26) + 16, 4) == 0
 
 
 def test_strerror(lib):
@@ -111,11 +117,11 @@ def test_gemv_validation(lib):
 
 def test_argmax_validation(lib):
     g = lib.nvfp4_gemv_argmax
-    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, B, 71, S0) == EWORKSPACE
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, B, 127, S0) == EWORKSPACE
     assert g(A, B, 1.0, 16, 32, C, 9, NULL, A, B, 1024, S0) == EINVAL   # argmax is n <= 8
-    assert g(A, B, 1.0, 16, 32, C, 4, NULL, NULL, B, 72, S0) == EINVAL
-    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, NULL, 72, S0) == EINVAL
-    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, ctypes.c_void_p(0x200004), 72, S0) == EALIGN
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, NULL, B, 128, S0) == EINVAL
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, NULL, 128, S0) == EINVAL
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, A, ctypes.c_void_p(0x200004), 128, S0) == EALIGN
 
 
 def test_other_entry_points_validation(lib):

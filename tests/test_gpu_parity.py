@@ -228,18 +228,19 @@ def test_argmax_matches_oracle(n):
 
 
 def test_argmax_workspace_reused_across_calls():
-    """The workspace returns to all-zero after each call, so back-to-back
-    calls on one workspace (different inputs and shapes) stay correct."""
+    """One workspace of garbage bytes, sized for the largest call, serves
+    back-to-back calls of different inputs and shapes."""
     import block_scaled_bit_nvfp4_amd as nv
-    wsp = torch.zeros(nv.nvfp4_gemv_argmax_workspace_bytes(8), dtype=torch.uint8, device=G.DEV)
-    for i, (R, K, n) in enumerate([(700, 512, 4), (300, 1024, 2), (1300, 512, 8), (700, 512, 4)]):
+    shapes = [(700, 512, 4), (300, 1024, 2), (1300, 512, 8), (700, 512, 4)]
+    size = max(nv.nvfp4_gemv_argmax_workspace_bytes(R, K, n) for R, K, n in shapes)
+    wsp = torch.full((size,), 0xFF, dtype=torch.uint8, device=G.DEV)
+    for i, (R, K, n) in enumerate(shapes):
         wq, ws, c_ref, s_ref = _prepare(R, K, 100 + R)
         X = G.seeded_x(n, K, seed=200 + i)
         G.note("argmax workspace reuse call %d" % i)
         _, am = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, X, with_logits=False, workspace=wsp)
         Y_ref, _ = oracle.gemv(c_ref, s_ref, 1.0, G.wl.bf16_bits(X))
         assert list(am.cpu().numpy()) == list(oracle.argmax_first(Y_ref)), i
-        assert torch.count_nonzero(wsp).item() == 0
 
 
 def test_argmax_ties_take_lowest_index():
