@@ -324,7 +324,7 @@ def main():
     if kernel == "gemm":
         achieved = step.flops / n_launch / per_launch_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(args.workload)}
     else:
         achieved = per_launch_bytes / per_launch_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
