@@ -255,9 +255,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, variant=None):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if absent or taken on different kernel sources."""
+    summary, or None if absent, taken on different kernel sources, or taken
+    on another variant of the step (the counters were collected on the
+    default one)."""
+    if variant:
+        return None
     p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(p):
         return None
@@ -328,7 +332,8 @@ def main():
     else:
         achieved = per_launch_bytes / per_launch_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(args.workload, "three launches" if args.mlp_three_launches else None)}
     roof["kernel_avg_us"] = round(per_launch_s * 1e6, 3)
     roof["scope"] = scope
 
