@@ -59,6 +59,12 @@ __device__ __forceinline__ float e4m3_f32(uint32_t word) {
     return __builtin_amdgcn_cvt_f32_fp8(word, Byte);
 }
 
+// E4M3 bytes 2 hi, 2 hi + 1 of `word` -> two exact fp32 (one v_cvt_pk_f32_fp8).
+__device__ __forceinline__ float2 e4m3x2_f32(uint32_t word, int hi) {
+    const auto v = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(word, true) : __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
+    return float2{v[0], v[1]};
+}
+
 __device__ __forceinline__ float e4m3_f32_dyn(uint32_t word, int byte) {
     switch (byte & 3) {
         case 0: return e4m3_f32<0>(word);

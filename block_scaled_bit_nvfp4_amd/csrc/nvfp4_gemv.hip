@@ -57,7 +57,9 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
               int kb, int ksplit, const uint16_t *__restrict__ X, int K, float *__restrict__ Y,
               unsigned long long *__restrict__ amax_ws, int32_t *__restrict__ argmax_out, int up_st,
               uint16_t *__restrict__ h) {
-    extern __shared__ float red[];   // [waves][N][SEG]
+    // [waves][narrow_wave_lds_bytes(N)] activation slots, then the partial
+    // sums [waves][N][SEG]
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int GPS = kSuperTiles / TWW;   // workgroups per super-tile
     constexpr int SEG = TWW * kTileRows;     // rows per workgroup
     constexpr int H = N > 4 ? 2 : 1;
@@ -67,9 +69,12 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
     const int half = MODE == kSwiglu ? wave / ksplit : 0;
     const int part = MODE == kSwiglu ? wave % ksplit : wave;
     const int o0 = int(int64_t(octets) * part / ksplit), o1 = int(int64_t(octets) * (part + 1) / ksplit);
+    constexpr int WL = narrow_wave_lds_bytes(N);
+    float *const red = reinterpret_cast<float *>(lds + int(blockDim.x >> 6) * WL);
 
     float acc[TWW][H];
-    narrow_accumulate<N, TWW>(wq, ws, int64_t(st) + (half ? up_st : 0), tg, o0, o1, octets, kb, X, K, lane, acc);
+    narrow_accumulate<N, TWW>(wq, ws, int64_t(st) + (half ? up_st : 0), tg, o0, o1, octets, kb, X, K, lane, acc,
+                              lds + wave * WL);
     {
         const int g = lane >> 4, r = lane & 15;
 #pragma unroll
@@ -171,7 +176,7 @@ int launch_narrow_tww(const Geometry &g, const NarrowConfig &cfg, const uint8_t 
                       float tscale, const uint16_t *X, int n, float *Y, unsigned long long *amax_ws,
                       int32_t *argmax_out, int up_st, uint16_t *h, int waves, int64_t groups, hipStream_t stream) {
     const dim3 grid{unsigned(groups)}, block{unsigned(kLanes * waves)};
-    const size_t lds = size_t(waves) * n * TWW * kTileRows * sizeof(float);
+    const size_t lds = size_t(waves) * (size_t(narrow_wave_lds_bytes(n)) + size_t(n) * TWW * kTileRows * sizeof(float));
     const int rows = int(g.rows), octets = int(g.octets), kb = int(g.kb), K = int(g.cols);
 #define NVFP4_LAUNCH(NN)                                                                                      \
     hipLaunchKernelGGL((narrow_kernel<NN, TWW, MODE>), grid, block, lds, stream, wq, ws, tscale, rows, octets, \

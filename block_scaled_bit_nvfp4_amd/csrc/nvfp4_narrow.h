@@ -28,9 +28,16 @@
 // row's octets (8 blocks) over `ksplit` waves; each wave streams its octets
 // with range-checked buffer loads, one octet ahead of the MFMAs: per tile one
 // 16-byte code load (the tile's 1 KiB chunk), the scales of its rows, and one
-// compact 16-byte activation load that v_ds_bpermute_b32 spreads into the A
-// operand.  Loads past the wave's last octet read zeros with no memory
-// traffic, so the loop needs no branch around a load.
+// compact 16-byte activation load per four columns.  Loads past the wave's
+// last octet read zeros with no memory traffic, so the loop needs no branch
+// around a load.
+//
+// A operands: the wave writes the octet's compact activations to its own LDS
+// slot and reads each A operand back with one ds_read_b128 per 32-k slice:
+// an active lane reads its column's 8 values, an inactive lane (slot of the
+// other block parity, or a column >= n) reads a 256-byte run of zeros kept in
+// the same wave-private region.  No workgroup barrier is involved: LDS
+// operations of one wave complete in order.
 #pragma once
 
 #include "nvfp4_host.h"
@@ -44,10 +51,17 @@ constexpr int kMaxKsplit = 16;
 constexpr int64_t kMaxNarrowCols = int64_t(1) << 26;
 
 // Decomposition of a rows x cols product over workgroups; a function of the
-// shape only.  Very tall matrices take whole super-tiles per workgroup (the
-// activation and scale loads are shared by four tiles), mid-size ones two
-// tiles, small ones one tile so that every CU gets work.  The k split aims at
-// about 8192 waves in all.
+// shape only.  Measured on the workload shapes (decode 4096 x 4096, the MLP's
+// 34816 x 5120 and 5120 x 17408, the 17408 x 5120 verify matrix and the
+// 151936 x 5120 vocabulary head): the narrow kernel keeps enough bytes in
+// flight with eight waves of two tiles per workgroup, except that
+//   - small matrices (<= 256 tiles) want one tile per workgroup and sixteen
+//     waves, so that every CU gets a workgroup and each wave a short chain;
+//   - mid-size ones (512 < tiles <= 4096) run best with one tile and eight
+//     waves, which also keeps the fused gate||up+SwiGLU workgroup (two sets of
+//     waves) at two workgroups per CU.
+// Shapes between 256 and 512 tiles take two tiles per workgroup so that the
+// workgroups (<= 256) stay one per CU instead of doubling up on some CUs.
 struct NarrowConfig {
     int tww;      // tiles per workgroup: 1, 2 or 4
     int ksplit;   // waves per workgroup (octet ranges)
@@ -56,15 +70,26 @@ struct NarrowConfig {
 
 inline NarrowConfig narrow_config(const Geometry &g) {
     NarrowConfig c;
-    c.tww = g.tiles >= 8192 ? 4 : (g.tiles * g.octets >= 32768 ? 2 : 1);
+    int k;
+    if (g.tiles <= 256) {
+        c.tww = 1;
+        k = 16;
+    } else if (g.tiles <= 512 || g.tiles > 4096) {
+        c.tww = 2;
+        k = 8;
+    } else {
+        c.tww = 1;
+        k = 8;
+    }
+    if (k > g.octets) k = int(g.octets);
+    c.ksplit = k < 1 ? 1 : k;
     c.groups = g.supertiles * (kSuperTiles / c.tww);
-    int64_t k = ceil_div(8192, c.groups);
-    if (k > kMaxKsplit) k = kMaxKsplit;
-    if (k > g.octets) k = g.octets;
-    if (k < 1) k = 1;
-    c.ksplit = int(k);
     return c;
 }
+
+// Bytes of LDS per wave of the narrow kernels: a 256-byte run of zeros, then
+// one slot of compact activations (1 KiB per four columns).
+constexpr int narrow_wave_lds_bytes(int n) { return 256 + (n > 4 ? 2 : 1) * 1024; }
 
 // Argmax key: order-preserving map of an fp32 value (with -0 folded into +0)
 // in the high word, the complement of the row index in the low word, so the
@@ -88,11 +113,12 @@ struct OctetData {
 
 // acc[tt][h]: this wave's share (octets [o0, o1)) of rows 16 (tile) + r of
 // tile tg * TWW + tt of super-tile st, for columns g + 4h (lane = 16g + r).
+// `wl` is the wave's private LDS region of narrow_wave_lds_bytes(N) bytes.
 template <int N, int TWW>
 __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws,
                                                   int64_t st, int tg, int o0, int o1, int octets, int kb,
                                                   const uint16_t *__restrict__ X, int K, int lane,
-                                                  float (&acc)[TWW][N > 4 ? 2 : 1]) {
+                                                  float (&acc)[TWW][N > 4 ? 2 : 1], uint8_t *wl) {
     constexpr int NC = N > 4 ? 2 : 1;
     constexpr int H = NC;
     const int g = lane >> 4, r = lane & 15;
@@ -112,10 +138,14 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
         const int c = xc + 4 * h;
         xvo[h] = c < N ? uint32_t((c * K + 32 * xp + 8 * xq) * 2) : kOutOfRange;
     }
-    // A-operand role of this lane: slot r of k-group g.
+    // LDS: [0, 256) zeros, then the slot: compact activations in lane order,
+    // i.e. column c's 128 values of the octet at 256 (c & 3) + 1024 (c >> 2).
+    reinterpret_cast<uint32_t *>(wl)[lane] = 0u;
+    u32x4 *const xslot = reinterpret_cast<u32x4 *>(wl + 256);
+    // A-operand role of this lane: slot r of k-group g, column cs.
     const int cs = (r >> 2) + 4 * ((r >> 1) & 1);
     const bool active = cs < N && (g >> 1) == (r & 1);
-    const int src = 4 * (16 * (cs & 3) + g);   // + 16p: byte address of the compact lane
+    const uint32_t aoff = active ? uint32_t(256 + (cs >> 2) * 1024 + (cs & 3) * 256 + 16 * g) : 0u;
 
     float part[TWW][H][2];
 #pragma unroll
@@ -139,6 +169,11 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
     };
 
     auto compute = [&](const OctetData<NC, TWW> &d) {
+#pragma unroll
+        for (int h = 0; h < NC; ++h) xslot[h * kLanes + lane] = d.x[h];
+        bf16x8 A[4];   // A operand of block pair p = 2-block slice 32p .. 32p + 31
+#pragma unroll
+        for (int p = 0; p < 4; ++p) A[p] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wl + aoff + 64 * p));
         uint32_t S[2][TWW];   // scale words (blocks 0..3, 4..7 of the octet) of each tile's row r
         if (TWW == 4) {
             uint32_t t0[4], t1[4];
@@ -157,32 +192,24 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
             }
         }
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            u32x4 av;
+        for (int tt = 0; tt < TWW; ++tt) {
+            // The tile's four MFMAs first, then the scale FMAs in block order:
+            // no FMA waits on the MFMA issued just before it.
+            floatx4 D[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t v = __builtin_amdgcn_ds_bpermute(src + 16 * p, d.x[0][j]);
-                if (NC == 2) {
-                    const uint32_t v2 = __builtin_amdgcn_ds_bpermute(src + 16 * p, d.x[NC - 1][j]);
-                    v = (cs >> 2) ? v2 : v;
-                }
-                av[j] = active ? v : 0u;
-            }
-            const bf16x8 a = __builtin_bit_cast(bf16x8, av);
+            for (int p = 0; p < 4; ++p)
+                D[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[p], e2m1x8_bf16(d.code[tt][p]),
+                                                            floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-            for (int tt = 0; tt < TWW; ++tt) {
-                const floatx4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, e2m1x8_bf16(d.code[tt][p]),
-                                                                        floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                const uint32_t sw = S[p >> 1][tt];
-                const float se = (p & 1) ? e4m3_f32<2>(sw) : e4m3_f32<0>(sw);   // block 2p of the octet
-                const float so = (p & 1) ? e4m3_f32<3>(sw) : e4m3_f32<1>(sw);   // block 2p + 1
+            for (int p = 0; p < 4; ++p) {
+                const float2 sc = e4m3x2_f32(S[p >> 1][tt], p & 1);   // blocks 2p, 2p + 1
                 float &a0 = part[tt][0][p & 1];
-                a0 = __builtin_fmaf(se, D[0], a0);
-                a0 = __builtin_fmaf(so, D[1], a0);
+                a0 = __builtin_fmaf(sc.x, D[p][0], a0);
+                a0 = __builtin_fmaf(sc.y, D[p][1], a0);
                 if (H == 2) {
                     float &a1 = part[tt][H - 1][p & 1];
-                    a1 = __builtin_fmaf(se, D[2], a1);
-                    a1 = __builtin_fmaf(so, D[3], a1);
+                    a1 = __builtin_fmaf(sc.x, D[p][2], a1);
+                    a1 = __builtin_fmaf(sc.y, D[p][3], a1);
                 }
             }
         }

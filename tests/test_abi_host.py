@@ -73,9 +73,11 @@ def test_plane_sizes_invalid(lib, rows, cols):
 def test_workspace_bytes(lib):
     # one 64-bit key per workgroup and column: a 16 x 32 matrix runs 4
     # one-tile workgroups (its 64-row super-tile), the 151936 x 5120 vocabulary
-    # projection 2374 four-tile workgroups
+    # projection (9496 tiles) 4748 two-tile workgroups, the 17408 x 5120
+    # matrix (1088 tiles) 1088 one-tile workgroups
     assert [nv.nvfp4_gemv_argmax_workspace_bytes(16, 32, n) for n in (0, 1, 4, 8, 9)] == [0, 32, 128, 256, 0]
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 4) == 2374 * 4 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 4) == 4748 * 4 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 1) == 1088 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, 24, 4) == 0
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, (1 << 26) + 16, 4) == 0
 
