@@ -38,6 +38,8 @@
 // workgroups of one XCD (workgroup b runs on XCD b mod 8), so a row group's
 // weights are fetched from HBM into that XCD's L2 once and re-read there by
 // the other column tiles.
+#include <type_traits>
+
 #include "nvfp4_host.h"
 
 namespace nvfp4 {
@@ -186,17 +188,25 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
 #pragma unroll
     for (int d = 0; d < 4; ++d) boff[d] = xtile_offset(c16, 4 * d + g);
 
-    auto compute = [&](int o) {
+    // The extra tile's B operands: this wave's quarter, column subtiles
+    // 2 wave and 2 wave + 1.
+    const uint32_t xboff = uint32_t(kExtraSub * wave * 16 * kXColBytes);
+
+    auto compute = [&](int o, auto extra_c) {
+        constexpr bool EXTRA = decltype(extra_c)::value;   // wave-uniform, fixed per workgroup
         const uint8_t *wst = wring + (o % kWRing) * kWStage;
-        u32x4 code[kSuperTiles];
+        u32x4 code[kSuperTiles], xcode = {};
 #pragma unroll
         for (int tt = 0; tt < kSuperTiles; ++tt)
             code[tt] = *reinterpret_cast<const u32x4 *>(wst + kWCode + tt * kCodeChunk + lane * 16);
-        const u32x4 xcode = *reinterpret_cast<const u32x4 *>(wst + kWXCode + lane * 16);
         const uint32_t scl = *reinterpret_cast<const uint32_t *>(wst + kWScaleLo + lane * 4);
         const uint32_t sch = *reinterpret_cast<const uint32_t *>(wst + kWScaleHi + lane * 4);
-        const uint32_t xs0 = *reinterpret_cast<const uint32_t *>(wst + kWXScale + c16 * 8);
-        const uint32_t xs1 = *reinterpret_cast<const uint32_t *>(wst + kWXScale + c16 * 8 + 4);
+        uint32_t xs0 = 0, xs1 = 0;
+        if (EXTRA) {
+            xcode = *reinterpret_cast<const u32x4 *>(wst + kWXCode + lane * 16);
+            xs0 = *reinterpret_cast<const uint32_t *>(wst + kWXScale + c16 * 8);
+            xs1 = *reinterpret_cast<const uint32_t *>(wst + kWXScale + c16 * 8 + 4);
+        }
         uint32_t s0[4], s1[4];   // scale words (blocks 0..3, 4..7) of row r of each tile
         gather_lane_groups(scl, s0);
         gather_lane_groups(sch, s1);
@@ -210,33 +220,44 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
         auto read_b = [&](int d, int cs) {
             return *reinterpret_cast<const bf16x8 *>(xb + cs * 16 * kXColBytes + boff[d]);
         };
+        auto read_xb = [&](int d, int e) {
+            return *reinterpret_cast<const bf16x8 *>(xb + xboff + e * 16 * kXColBytes + boff[d]);
+        };
         // Software pipeline over the four 32-k slices: slice d + 1's A
         // operands are decoded between slice d's MFMAs (one tile per two
         // column subtiles), and each B operand is re-read for slice d + 1 as
-        // soon as slice d's MFMAs have issued with it.
-        bf16x8 a[kSuperTiles], an[kSuperTiles], xa = {}, xan = {}, bv[kWideSub];
+        // soon as slice d's MFMAs have issued with it.  No branch inside, so
+        // the scheduler can interleave the decode with the MFMAs.
+        // a[d & 1]: slice d's A operands; slice d + 1's go to the other half,
+        // so no register copies between slices.
+        bf16x8 a[2][kSuperTiles], xa[2] = {}, bv[kWideSub], xbv[kExtraSub];
 #pragma unroll
         for (int cs = 0; cs < kWideSub; ++cs) bv[cs] = read_b(0, cs);
 #pragma unroll
-        for (int tt = 0; tt < kSuperTiles; ++tt) a[tt] = decode(0, tt);
-        if (has_extra) xa = xdecode(0);
+        for (int tt = 0; tt < kSuperTiles; ++tt) a[0][tt] = decode(0, tt);
+        if (EXTRA) {
+            xa[0] = xdecode(0);
+#pragma unroll
+            for (int e = 0; e < kExtraSub; ++e) xbv[e] = read_xb(0, e);
+        }
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
+            const int cur = d & 1, nxt = cur ^ 1;
 #pragma unroll
             for (int cs = 0; cs < kWideSub; ++cs) {
 #pragma unroll
                 for (int tt = 0; tt < kSuperTiles; ++tt)
-                    acc[tt][cs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[tt], bv[cs], acc[tt][cs], 0, 0, 0);
-                if (has_extra && (cs >> 1) == wave)   // this wave's quarter of the extra tile
-                    xacc[cs & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bv[cs], xacc[cs & 1], 0, 0, 0);
+                    acc[tt][cs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[cur][tt], bv[cs], acc[tt][cs], 0, 0, 0);
                 if (d < 3) bv[cs] = read_b(d + 1, cs);
-                if (d < 3 && (cs & 1)) an[cs >> 1] = decode(d + 1, cs >> 1);
+                if (d < 3 && (cs & 1)) a[nxt][cs >> 1] = decode(d + 1, cs >> 1);
             }
-            if (d < 3) {
+            if (EXTRA) {
 #pragma unroll
-                for (int tt = 0; tt < kSuperTiles; ++tt) a[tt] = an[tt];
-                if (has_extra) xan = xdecode(d + 1);
-                xa = xan;
+                for (int e = 0; e < kExtraSub; ++e) {
+                    xacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cur], xbv[e], xacc[e], 0, 0, 0);
+                    if (d < 3) xbv[e] = read_xb(d + 1, e);
+                }
+                if (d < 3) xa[nxt] = xdecode(d + 1);
             }
         }
     };
@@ -250,17 +271,21 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
     // bare barrier: __syncthreads() would also drain every outstanding load
     // (its fence), emptying the rings; the memory clobber keeps the LDS reads
     // below it.
-    load_w(0);
-    stage_x(0);
-    if (octets > 1) load_w(1);
-    for (int o = 0; o < octets; ++o) {
-        if (o + 1 < octets) __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads));
-        else __builtin_amdgcn_s_waitcnt(0);
-        asm volatile("s_barrier" ::: "memory");
-        if (o + 1 < octets) stage_x(o + 1);
-        if (o + 2 < octets) load_w(o + 2);
-        compute(o);
-    }
+    auto run = [&](auto extra_c) {
+        load_w(0);
+        stage_x(0);
+        if (octets > 1) load_w(1);
+        for (int o = 0; o < octets; ++o) {
+            if (o + 1 < octets) __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads));
+            else __builtin_amdgcn_s_waitcnt(0);
+            asm volatile("s_barrier" ::: "memory");
+            if (o + 1 < octets) stage_x(o + 1);
+            if (o + 2 < octets) load_w(o + 2);
+            compute(o, extra_c);
+        }
+    };
+    if (has_extra) run(std::true_type{});
+    else run(std::false_type{});
 
     // Lane (g, c16) holds rows 4g .. 4g + 3 of a tile for column
     // cs * 16 + c16 of the column tile.
