@@ -11,26 +11,27 @@
 // multiplied on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the tensor
 // scale multiplies the result.
 //
-// Tiling.  One wave per SIMD (the whole register file: accumulators in
-// AGPRs, operand pipelines in VGPRs).  A wave owns one 64-row super-tile x
-// 128 activation columns over the whole K; a workgroup's four waves share
-// one 128-column tile of X, staged in LDS one octet (128 k) at a time through
-// a ring of three buffers: direct-to-LDS buffer loads two octets ahead of
-// the MFMAs, XOR-swizzled by 16-byte chunk so that the B-operand reads of 16
-// neighbouring columns hit distinct banks.  Weights never touch LDS: per
-// octet a lane loads its 16-byte code entry of each tile and one 8-byte scale
-// entry (spread to the other lane groups with v_permlane swaps), two octets
-// ahead, and decodes in registers: word d of a tile's entry is directly the A
+// Tiling.  Two waves per SIMD, so that one wave's weight decode (VALU) runs
+// while the other's MFMAs execute.  A workgroup of eight waves owns four
+// 64-row super-tiles x 128 activation columns; wave w takes two tiles
+// (32 rows) of super-tile w / 2 over all 128 columns (64 fp32 accumulators
+// per lane, in AGPRs).  The workgroup's X tile (128 columns) is staged in
+// LDS one octet (128 k) at a time through a ring of two buffers by
+// direct-to-LDS buffer loads, XOR-swizzled by 16-byte chunk so that the
+// B-operand reads of 16 neighbouring columns hit distinct banks; the weights
+// go the same way into a ring of three stages, two octets ahead of the
+// MFMAs.  Word d of a lane's 16-byte code entry of a tile is directly the A
 // operand of k = 128o + 32d .. +31 (lane 16g + r: row r, elements
-// 8g .. 8g + 7).  A decoded A operand feeds eight MFMAs (the column
-// subtiles); the next slice's A operands are decoded, and each B operand is
-// re-read for the next slice, between the current slice's MFMAs.
+// 8g .. 8g + 7), decoded to exact bf16 in registers with its E4M3 scale.  A
+// decoded A operand feeds eight MFMAs (the column subtiles); the next slice's
+// A operands are decoded, and each B operand is re-read for the next slice,
+// between the current slice's MFMAs.
 //
 // Balance.  When the super-tiles do not split evenly over the CUs (17408
 // rows = 272 super-tiles against 256 CUs at N = 512), the row groups are cut
 // back to a whole number of CU rounds and each workgroup also takes one of
-// the remaining tiles, its four waves one 32-column quarter each: every wave
-// then carries exactly the same work (4 x 128 + 32 tile-columns at N = 512).
+// the remaining tiles, its eight waves one 16-column subtile each: every wave
+// then carries exactly the same work (2 x 128 + 16 tile-columns at N = 512).
 // Each output's accumulation is the same MFMA chain whichever wave computes
 // it, so the decomposition does not change any result bit.
 //
@@ -44,21 +45,26 @@
 
 namespace nvfp4 {
 
-constexpr int kWideWaves = 4;                   // waves (super-tiles) per workgroup
+constexpr int kWideSupers = 4;                  // super-tiles per workgroup
+constexpr int kWaveTiles = 2;                   // tiles per wave
+constexpr int kWideWaves = kWideSupers * kSuperTiles / kWaveTiles;   // 8
 constexpr int kWideCols = 128;                  // activation columns per workgroup
-constexpr int kWideSub = kWideCols / 16;        // column subtiles of an MFMA
-constexpr int kExtraSub = kWideSub / kWideWaves;   // column subtiles of a wave's extra tile
+constexpr int kWideSub = kWideCols / 16;        // column subtiles of an MFMA (one per wave for the extra tile)
 constexpr int kXColBytes = kOctet * kBlock * 2; // one column's octet: 128 bf16
 constexpr int kXBuf = kWideCols * kXColBytes;   // one octet of the X tile: 32 KiB
 constexpr int kXRing = 2;                       // octets of X in LDS
 constexpr int kXDmaPerWave = kXBuf / (kWideWaves * kLanes * 16);   // 16-byte lanes
-// A wave's weights of one octet in LDS: the super-tile's four code chunks,
-// the extra tile's code chunk, the super-tile's scale entry as two dword
-// planes and the extra tile's 128 scale bytes.
-constexpr int kWCode = 0, kWXCode = 4096, kWScaleLo = 5120, kWScaleHi = 5376, kWXScale = 5632;
-constexpr int kWStage = 6144;
+// One octet of the workgroup's weights in LDS: per wave its two code chunks
+// and its tiles' scale bytes as two dword planes; then the extra tile's
+// code chunk and scale bytes, and a scratch run for the placeholder loads
+// that keep every wave's load count equal.
+constexpr int kWWave = kWaveTiles * kCodeChunk + 2 * 256;   // 2.5 KiB
+constexpr int kWXCode = kWideWaves * kWWave;
+constexpr int kWXScale = kWXCode + kCodeChunk;
+constexpr int kWDummy = kWXScale + 256;
+constexpr int kWStage = kWDummy + 256;
 constexpr int kWRing = 3;                       // octets of weights in LDS
-constexpr int kWideLds = kXRing * kXBuf + kWRing * kWideWaves * kWStage;   // 136 KiB
+constexpr int kWideLds = kXRing * kXBuf + kWRing * kWStage;
 constexpr int kXcds = 8;
 // Longest rows of the wide product: a column tile of X and a super-tile's
 // code stream stay below 2^31 bytes of buffer offset.
@@ -104,11 +110,11 @@ struct WideConfig {
     int64_t groups;   // launched workgroups (whole XCD rounds; the excess leaves at once)
 };
 
-__global__ void __launch_bounds__(kWideWaves * kLanes, 1)
+__global__ void __launch_bounds__(kWideWaves * kLanes, 2)
 wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows, int supertiles,
             int octets, int K, const uint16_t *__restrict__ X, int n, float *__restrict__ Y, int row_groups,
             int col_groups, int extra, int vec_store) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // X ring, then the weight rings
+    extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // X ring, then the weight ring
     asm volatile("" ::: "a0");   // lets the accumulators live in AGPRs
 
     // Workgroup -> (row group, column tile): the column tiles of a row group
@@ -124,15 +130,18 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
     const int n0 = cg * kWideCols;
     const int c16 = lane & 15, g = lane >> 4;
 
-    // This wave's super-tile; one past the last reads zeros and stores nothing.
-    const int unit = rg * kWideWaves + wave;
+    // This wave's tiles: 2 half, 2 half + 1 of super-tile unit; a super-tile
+    // past the last reads zeros and stores nothing.
+    const int unit = rg * kWideSupers + (wave >> 1);
+    const int half = wave & 1;
     const bool has_unit = unit < supertiles;
     const int64_t ubase = int64_t(has_unit ? unit : 0) * octets;
-    const auto crs = make_rsrc(wq + ubase * kCodeRegion, has_unit ? uint32_t(octets) * kCodeRegion : 0u);
-    const auto srs = make_rsrc(ws + ubase * kScaleRegion, has_unit ? uint32_t(octets) * kScaleRegion : 0u);
-    // The extra tile of this workgroup (the same for its four waves, each
-    // taking column subtiles 2 wave, 2 wave + 1 of it).
-    const int xtile = row_groups * kWideWaves * kSuperTiles + rg;
+    const auto crs = make_rsrc(wq + ubase * kCodeRegion + half * kWaveTiles * kCodeChunk,
+                               has_unit ? uint32_t(octets) * kCodeRegion : 0u);
+    const auto srs = make_rsrc(ws + ubase * kScaleRegion + half * kWaveTiles * kScaleChunk,
+                               has_unit ? uint32_t(octets) * kScaleRegion : 0u);
+    // The extra tile of this workgroup (each wave takes column subtile wave).
+    const int xtile = row_groups * kWideSupers * kSuperTiles + rg;
     const bool has_extra = rg < extra && xtile < supertiles * kSuperTiles;
     const int64_t xbase = has_extra ? int64_t(xtile >> 2) * octets : 0;
     const auto xcrs = make_rsrc(wq + xbase * kCodeRegion + (xtile & 3) * kCodeChunk,
@@ -142,6 +151,7 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
     // This workgroup's columns of X; columns past n read zeros.
     const int ncols = n - n0 < kWideCols ? n - n0 : kWideCols;
     const auto xrs = make_rsrc(X + int64_t(n0) * K, uint32_t(ncols) * uint32_t(K) * 2u);
+    auto lds_ptr = [](uint8_t *p) { return (__attribute__((address_space(3))) void *)p; };
 
     // Direct-to-LDS staging: LDS chunk p = (wave * kXDmaPerWave + i) * 64 +
     // lane of a buffer holds column p >> 4, k-chunk (p & 15) ^ (column & 15).
@@ -152,62 +162,68 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
             const int p = (wave * kXDmaPerWave + i) * kLanes + lane;
             const int c = p >> 4, j = (p & 15) ^ (c & 15);
             const uint32_t off = (o * 128 + 8 * j < K) ? uint32_t(c * K + o * 128 + 8 * j) * 2u : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (__attribute__((address_space(3))) void *)(dst + i * 1024),
-                                                     16, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, lds_ptr(dst + i * 1024), 16, off, 0, 0, 0);
         }
     };
-    // Weights of octet o into this wave's ring stage o % 3 (direct-to-LDS).
-    uint8_t *const wring = xs + kXRing * kXBuf + wave * kWRing * kWStage;
-    auto lds_ptr = [](uint8_t *p) { return (__attribute__((address_space(3))) void *)p; };
+    // Weights of octet o into ring stage o % 3: this wave's two code chunks
+    // (lane l's 16 bytes of tile j at 1024 j + 16 l), its tiles' 256 scale
+    // bytes as low and high dwords of lanes 0 .. 31 (lane 16 j + r: row r of
+    // tile j), and one of the extra tile's code chunk, its scale bytes, or a
+    // placeholder load.
+    uint8_t *const wring = xs + kXRing * kXBuf;
     auto load_w = [&](int o) {
         uint8_t *dst = wring + (o % kWRing) * kWStage;
+        uint8_t *mine = dst + wave * kWWave;
         const uint32_t co = uint32_t(o) * kCodeRegion + uint32_t(lane) * 16u;
 #pragma unroll
-        for (int tt = 0; tt < kSuperTiles; ++tt)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, lds_ptr(dst + kWCode + tt * kCodeChunk), 16, co + tt * kCodeChunk,
-                                                     0, 0, kStream);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xcrs, lds_ptr(dst + kWXCode), 16, co, 0, 0, kStream);
-        const uint32_t so = uint32_t(o) * kScaleRegion + uint32_t(lane) * 8u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(dst + kWScaleLo), 4, so, 0, 0, kStream);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(dst + kWScaleHi), 4, so + 4, 0, 0, kStream);
-        const uint32_t xso = lane < 32 ? uint32_t(o) * kScaleRegion + uint32_t(lane) * 4u : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(dst + kWXScale), 4, xso, 0, 0, kStream);
+        for (int j = 0; j < kWaveTiles; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, lds_ptr(mine + j * kCodeChunk), 16, co + j * kCodeChunk, 0, 0,
+                                                     kStream);
+        const uint32_t so = lane < 32 ? uint32_t(o) * kScaleRegion + uint32_t(lane) * 8u : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk), 4, so, 0, 0, kStream);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk + 256), 4,
+                                                 so == kOutOfRange ? so : so + 4, 0, 0, kStream);
+        if (wave == 0) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xcrs, lds_ptr(dst + kWXCode), 16, co, 0, 0, kStream);
+        } else if (wave == 1) {
+            const uint32_t xso = lane < 32 ? uint32_t(o) * kScaleRegion + uint32_t(lane) * 4u : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(dst + kWXScale), 4, xso, 0, 0, kStream);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(dst + kWDummy), 4, kOutOfRange, 0, 0, kStream);
+        }
     };
-    constexpr int kWLoads = kSuperTiles + 4;   // vector-memory operations of load_w
+    constexpr int kWLoads = kWaveTiles + 3;   // vector-memory operations of load_w per wave
 
-    floatx4 acc[kSuperTiles][kWideSub], xacc[kExtraSub];
+    floatx4 acc[kWaveTiles][kWideSub], xacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tt = 0; tt < kSuperTiles; ++tt)
+    for (int tt = 0; tt < kWaveTiles; ++tt)
 #pragma unroll
         for (int cs = 0; cs < kWideSub; ++cs) acc[tt][cs] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < kExtraSub; ++e) xacc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // B-operand chunk offsets of this lane for each 32-k slice d.
+    // B-operand chunk offsets of this lane for each 32-k slice d; the extra
+    // tile's column subtile is this wave's.
     uint32_t boff[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) boff[d] = xtile_offset(c16, 4 * d + g);
-
-    // The extra tile's B operands: this wave's quarter, column subtiles
-    // 2 wave and 2 wave + 1.
-    const uint32_t xboff = uint32_t(kExtraSub * wave * 16 * kXColBytes);
+    const uint32_t xboff = uint32_t(wave * 16 * kXColBytes);
 
     auto compute = [&](int o, auto extra_c) {
         constexpr bool EXTRA = decltype(extra_c)::value;   // wave-uniform, fixed per workgroup
         const uint8_t *wst = wring + (o % kWRing) * kWStage;
-        u32x4 code[kSuperTiles], xcode = {};
+        const uint8_t *mine = wst + wave * kWWave;
+        u32x4 code[kWaveTiles], xcode = {};
 #pragma unroll
-        for (int tt = 0; tt < kSuperTiles; ++tt)
-            code[tt] = *reinterpret_cast<const u32x4 *>(wst + kWCode + tt * kCodeChunk + lane * 16);
-        const uint32_t scl = *reinterpret_cast<const uint32_t *>(wst + kWScaleLo + lane * 4);
-        const uint32_t sch = *reinterpret_cast<const uint32_t *>(wst + kWScaleHi + lane * 4);
+        for (int tt = 0; tt < kWaveTiles; ++tt)
+            code[tt] = *reinterpret_cast<const u32x4 *>(mine + tt * kCodeChunk + lane * 16);
+        const uint32_t scl = *reinterpret_cast<const uint32_t *>(mine + kWaveTiles * kCodeChunk + lane * 4);
+        const uint32_t sch = *reinterpret_cast<const uint32_t *>(mine + kWaveTiles * kCodeChunk + 256 + lane * 4);
         uint32_t xs0 = 0, xs1 = 0;
         if (EXTRA) {
             xcode = *reinterpret_cast<const u32x4 *>(wst + kWXCode + lane * 16);
             xs0 = *reinterpret_cast<const uint32_t *>(wst + kWXScale + c16 * 8);
             xs1 = *reinterpret_cast<const uint32_t *>(wst + kWXScale + c16 * 8 + 4);
         }
-        uint32_t s0[4], s1[4];   // scale words (blocks 0..3, 4..7) of row r of each tile
+        uint32_t s0[4], s1[4];   // scale words (blocks 0..3, 4..7) of row r of each of the wave's tiles
         gather_lane_groups(scl, s0);
         gather_lane_groups(sch, s1);
         const uint8_t *xb = xs + (o % kXRing) * kXBuf;
@@ -220,25 +236,20 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
         auto read_b = [&](int d, int cs) {
             return *reinterpret_cast<const bf16x8 *>(xb + cs * 16 * kXColBytes + boff[d]);
         };
-        auto read_xb = [&](int d, int e) {
-            return *reinterpret_cast<const bf16x8 *>(xb + xboff + e * 16 * kXColBytes + boff[d]);
-        };
-        // Software pipeline over the four 32-k slices: slice d + 1's A
-        // operands are decoded between slice d's MFMAs (one tile per two
-        // column subtiles), and each B operand is re-read for slice d + 1 as
-        // soon as slice d's MFMAs have issued with it.  No branch inside, so
-        // the scheduler can interleave the decode with the MFMAs.
-        // a[d & 1]: slice d's A operands; slice d + 1's go to the other half,
-        // so no register copies between slices.
-        bf16x8 a[2][kSuperTiles], xa[2] = {}, bv[kWideSub], xbv[kExtraSub];
+        auto read_xb = [&](int d) { return *reinterpret_cast<const bf16x8 *>(xb + xboff + boff[d]); };
+        // Software pipeline over the four 32-k slices: a[d & 1] holds slice
+        // d's A operands, slice d + 1's are decoded into the other half
+        // between slice d's MFMAs, and each B operand is re-read for slice
+        // d + 1 as soon as slice d's MFMAs have issued with it.  No branch
+        // inside, so the scheduler can interleave decode and MFMAs.
+        bf16x8 a[2][kWaveTiles], xa[2] = {}, bv[kWideSub], xbv = {};
 #pragma unroll
         for (int cs = 0; cs < kWideSub; ++cs) bv[cs] = read_b(0, cs);
 #pragma unroll
-        for (int tt = 0; tt < kSuperTiles; ++tt) a[0][tt] = decode(0, tt);
+        for (int tt = 0; tt < kWaveTiles; ++tt) a[0][tt] = decode(0, tt);
         if (EXTRA) {
             xa[0] = xdecode(0);
-#pragma unroll
-            for (int e = 0; e < kExtraSub; ++e) xbv[e] = read_xb(0, e);
+            xbv = read_xb(0);
         }
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -246,18 +257,17 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
 #pragma unroll
             for (int cs = 0; cs < kWideSub; ++cs) {
 #pragma unroll
-                for (int tt = 0; tt < kSuperTiles; ++tt)
+                for (int tt = 0; tt < kWaveTiles; ++tt)
                     acc[tt][cs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[cur][tt], bv[cs], acc[tt][cs], 0, 0, 0);
                 if (d < 3) bv[cs] = read_b(d + 1, cs);
-                if (d < 3 && (cs & 1)) a[nxt][cs >> 1] = decode(d + 1, cs >> 1);
+                if (d < 3 && (cs & 3) == 3) a[nxt][cs >> 2] = decode(d + 1, cs >> 2);
             }
             if (EXTRA) {
-#pragma unroll
-                for (int e = 0; e < kExtraSub; ++e) {
-                    xacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cur], xbv[e], xacc[e], 0, 0, 0);
-                    if (d < 3) xbv[e] = read_xb(d + 1, e);
+                xacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cur], xbv, xacc, 0, 0, 0);
+                if (d < 3) {
+                    xbv = read_xb(d + 1);
+                    xa[nxt] = xdecode(d + 1);
                 }
-                if (d < 3) xa[nxt] = xdecode(d + 1);
             }
         }
     };
@@ -266,10 +276,10 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
     // octet o a wave issues octet o + 1's X loads, then octet o + 2's weight
     // loads, so at the start of octet o + 1 only the latter may still be
     // outstanding: the wait below finishes this wave's loads of the octet
-    // about to be used, and the barrier publishes every wave's share of the
-    // X tile and frees the buffers restaged next (read at octet o - 1).  A
-    // bare barrier: __syncthreads() would also drain every outstanding load
-    // (its fence), emptying the rings; the memory clobber keeps the LDS reads
+    // about to be used, and the barrier publishes every wave's loads and
+    // frees the buffers restaged next (read at octet o - 1).  A bare
+    // barrier: __syncthreads() would also drain every outstanding load (its
+    // fence), emptying the rings; the memory clobber keeps the LDS reads
     // below it.
     auto run = [&](auto extra_c) {
         load_w(0);
@@ -302,16 +312,13 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
     };
     if (has_unit) {
 #pragma unroll
-        for (int tt = 0; tt < kSuperTiles; ++tt)
+        for (int tt = 0; tt < kWaveTiles; ++tt)
 #pragma unroll
             for (int cs = 0; cs < kWideSub; ++cs)
-                store(acc[tt][cs], unit * kSuperRows + tt * kTileRows + 4 * g, n0 + cs * 16 + c16);
+                store(acc[tt][cs], unit * kSuperRows + (half * kWaveTiles + tt) * kTileRows + 4 * g,
+                      n0 + cs * 16 + c16);
     }
-    if (has_extra) {
-#pragma unroll
-        for (int e = 0; e < kExtraSub; ++e)
-            store(xacc[e], xtile * kTileRows + 4 * g, n0 + (kExtraSub * wave + e) * 16 + c16);
-    }
+    if (has_extra) store(xacc, xtile * kTileRows + 4 * g, n0 + wave * 16 + c16);
 }
 
 // The decomposition: workgroups of four super-tiles per 128-column tile.
@@ -321,14 +328,14 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
 inline WideConfig wide_config(const Geometry &g, int n, int cus) {
     WideConfig c;
     c.col_groups = int(ceil_div(n, kWideCols));
-    c.row_groups = int(ceil_div(g.supertiles, kWideWaves));
+    c.row_groups = int(ceil_div(g.supertiles, kWideSupers));
     c.extra = 0;
     if (cus > 0 && cus % c.col_groups == 0) {
         const int64_t per_round = cus / c.col_groups;                  // row groups per CU round
-        const int64_t rounds = (g.supertiles / kWideWaves) / per_round;
+        const int64_t rounds = (g.supertiles / kWideSupers) / per_round;
         if (rounds >= 1) {
             const int64_t rg = rounds * per_round;
-            const int64_t left_tiles = (g.supertiles - rg * kWideWaves) * kSuperTiles;
+            const int64_t left_tiles = (g.supertiles - rg * kWideSupers) * kSuperTiles;
             if (left_tiles > 0 && left_tiles <= rg) {
                 c.row_groups = int(rg);
                 c.extra = int(left_tiles);
