@@ -135,21 +135,33 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
 // Second launch of the argmax: the product's per-workgroup keys are complete
 // (kernel boundary); the largest key of each column names its row.  The
 // maximum is order-independent, so the result is exact and reproducible.
-constexpr int kFinishThreads = 256;
+// The keys were just written from every XCD, so each read goes to memory:
+// every thread issues the loads of up to kFinishUnroll groups before it
+// compares any of them, which keeps the reduction to one or two memory round
+// trips for up to 8192 groups instead of one per loop iteration.
+constexpr int kFinishThreads = 1024;
 
 template <int N>
 __global__ void __launch_bounds__(kFinishThreads)
 argmax_finish_kernel(const unsigned long long *__restrict__ keys, int groups, int32_t *__restrict__ argmax_out) {
+    constexpr int U = N > 4 ? 4 : 8;   // groups per thread per pass (register budget)
     __shared__ unsigned long long part[kFinishThreads / kLanes][N];
     unsigned long long m[N];
 #pragma unroll
     for (int c = 0; c < N; ++c) m[c] = 0ull;
-    for (int g = threadIdx.x; g < groups; g += kFinishThreads)
+    for (int g0 = 0; g0 < groups; g0 += kFinishThreads * U) {
+        unsigned long long k[U][N];
 #pragma unroll
-        for (int c = 0; c < N; ++c) {
-            const unsigned long long k = keys[int64_t(g) * N + c];
-            m[c] = k > m[c] ? k : m[c];
+        for (int u = 0; u < U; ++u) {
+            const int g = g0 + u * kFinishThreads + int(threadIdx.x);
+#pragma unroll
+            for (int c = 0; c < N; ++c) k[u][c] = g < groups ? keys[int64_t(g) * N + c] : 0ull;
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < N; ++c) m[c] = k[u][c] > m[c] ? k[u][c] : m[c];
+    }
 #pragma unroll
     for (int c = 0; c < N; ++c) {
 #pragma unroll
