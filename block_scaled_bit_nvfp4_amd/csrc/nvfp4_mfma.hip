@@ -20,7 +20,8 @@
 // direct-to-LDS buffer loads, XOR-swizzled by 16-byte chunk so that the
 // B-operand reads of 16 neighbouring columns hit distinct banks; the weights
 // go the same way into a ring of three stages, two octets ahead of the
-// MFMAs.  Word d of a lane's 16-byte code entry of a tile is directly the A
+// MFMAs.  The two waves of a SIMD take turns at the higher issue priority
+// slice by slice, which keeps them level at the per-octet barrier.  Word d of a lane's 16-byte code entry of a tile is directly the A
 // operand of k = 128o + 32d .. +31 (lane 16g + r: row r, elements
 // 8g .. 8g + 7), decoded to exact bf16 in registers with its E4M3 scale.  A
 // decoded A operand feeds eight MFMAs (the column subtiles); the next slice's
@@ -31,9 +32,12 @@
 // rows = 272 super-tiles against 256 CUs at N = 512), the row groups are cut
 // back to a whole number of CU rounds and each workgroup also takes one of
 // the remaining tiles, its eight waves one 16-column subtile each: every wave
-// then carries exactly the same work (2 x 128 + 16 tile-columns at N = 512).
-// Each output's accumulation is the same MFMA chain whichever wave computes
-// it, so the decomposition does not change any result bit.
+// then carries the same MFMA work (2 x 128 + 16 tile-columns at N = 512).
+// The extra tile's A operands are decoded once per workgroup: waves 0..3
+// each decode one 32-k slice of the next octet (from their own copy of its
+// raw bytes) into a two-octet LDS ring that every wave reads.  Each output's
+// accumulation is the same MFMA chain whichever wave computes it, so the
+// decomposition does not change any result bit.
 //
 // Workgroup order.  The column tiles of one row group are consecutive
 // workgroups of one XCD (workgroup b runs on XCD b mod 8), so a row group's
@@ -55,16 +59,22 @@ constexpr int kXBuf = kWideCols * kXColBytes;   // one octet of the X tile: 32 K
 constexpr int kXRing = 2;                       // octets of X in LDS
 constexpr int kXDmaPerWave = kXBuf / (kWideWaves * kLanes * 16);   // 16-byte lanes
 // One octet of the workgroup's weights in LDS: per wave its two code chunks
-// and its tiles' scale bytes as two dword planes; then the extra tile's
-// code chunk and scale bytes, and a scratch run for the placeholder loads
-// that keep every wave's load count equal.
+// and its tiles' scale bytes as two dword planes; then, for each of the
+// waves that decode the extra tile (one 32-k slice each), its own copy of
+// the extra tile's code chunk and scale bytes; and a scratch run for the
+// placeholder loads that keep every wave's load count equal.
 constexpr int kWWave = kWaveTiles * kCodeChunk + 2 * 256;   // 2.5 KiB
+constexpr int kXDecoders = 4;                   // waves decoding the extra tile, one slice each
+constexpr int kWXWave = kCodeChunk + 256;       // a decoder's raw extra tile: code, then 128 scale bytes
 constexpr int kWXCode = kWideWaves * kWWave;
-constexpr int kWXScale = kWXCode + kCodeChunk;
-constexpr int kWDummy = kWXScale + 256;
+constexpr int kWDummy = kWXCode + kXDecoders * kWXWave;
 constexpr int kWStage = kWDummy + 256;
 constexpr int kWRing = 3;                       // octets of weights in LDS
-constexpr int kWideLds = kXRing * kXBuf + kWRing * kWStage;
+// The extra tile's decoded A operands of one octet: 4 slices x 64 lanes x
+// 16 bytes, in a ring of two octets.
+constexpr int kXABuf = 4 * kLanes * 16;
+constexpr int kXARing = 2;
+constexpr int kWideLds = kXRing * kXBuf + kWRing * kWStage + kXARing * kXABuf;
 constexpr int kXcds = 8;
 // Longest rows of the wide product: a column tile of X and a super-tile's
 // code stream stay below 2^31 bytes of buffer offset.
@@ -94,6 +104,8 @@ __device__ __forceinline__ bf16x8 decode_scaled(uint32_t word, float s) {
 // s_waitcnt immediate that waits until at most v vector-memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left alone).
 constexpr int vmcnt_only(int v) { return (v & 0xF) | ((v >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+// The same, and every LDS operation of this wave done.
+constexpr int vmcnt_lds(int v) { return (v & 0xF) | ((v >> 4) << 14) | (0x7 << 4); }
 
 // LDS byte offset of 16-byte chunk j (k = 8j .. 8j + 7 of the octet) of
 // column c of an X tile buffer.
@@ -168,9 +180,10 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
     // Weights of octet o into ring stage o % 3: this wave's two code chunks
     // (lane l's 16 bytes of tile j at 1024 j + 16 l), its tiles' 256 scale
     // bytes as low and high dwords of lanes 0 .. 31 (lane 16 j + r: row r of
-    // tile j), and one of the extra tile's code chunk, its scale bytes, or a
-    // placeholder load.
+    // tile j), and for a decoder wave its own copy of the extra tile's code
+    // chunk and scale bytes (two placeholder loads for the other waves).
     uint8_t *const wring = xs + kXRing * kXBuf;
+    uint8_t *const xaring = wring + kWRing * kWStage;
     auto load_w = [&](int o) {
         uint8_t *dst = wring + (o % kWRing) * kWStage;
         uint8_t *mine = dst + wave * kWWave;
@@ -183,16 +196,29 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
         __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk), 4, so, 0, 0, kStream);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk + 256), 4,
                                                  so == kOutOfRange ? so : so + 4, 0, 0, kStream);
-        if (wave == 0) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xcrs, lds_ptr(dst + kWXCode), 16, co, 0, 0, kStream);
-        } else if (wave == 1) {
+        if (wave < kXDecoders) {
+            uint8_t *xw = dst + kWXCode + wave * kWXWave;
             const uint32_t xso = lane < 32 ? uint32_t(o) * kScaleRegion + uint32_t(lane) * 4u : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(dst + kWXScale), 4, xso, 0, 0, kStream);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xcrs, lds_ptr(xw), 16, co, 0, 0, kStream);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(xw + kCodeChunk), 4, xso, 0, 0, kStream);
         } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(dst + kWDummy), 4, kOutOfRange, 0, 0, kStream);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(dst + kWDummy), 4, kOutOfRange, 0, 0, kStream);
         }
     };
-    constexpr int kWLoads = kWaveTiles + 3;   // vector-memory operations of load_w per wave
+    constexpr int kWLoads = kWaveTiles + 4;   // vector-memory operations of load_w per wave
+    // A decoder wave turns slice d = wave of the extra tile's octet o into
+    // exact bf16 A operands for every lane, from its own copy of the raw
+    // bytes, into the extra ring (published by the next barrier).
+    auto decode_extra = [&](int o) {
+        const uint8_t *xw = wring + (o % kWRing) * kWStage + kWXCode + wave * kWXWave;
+        const int d = wave;
+        const uint32_t word = *reinterpret_cast<const uint32_t *>(xw + lane * 16 + d * 4);
+        const uint32_t sw = *reinterpret_cast<const uint32_t *>(xw + kCodeChunk + c16 * 8 + (d < 2 ? 0 : 4));
+        const float sc = e4m3_f32<0>(sw >> (8 * ((2 * d + (g >> 1)) & 3)));
+        *reinterpret_cast<bf16x8 *>(xaring + (o % kXARing) * kXABuf + d * kLanes * 16 + lane * 16) =
+            decode_scaled(word, sc);
+    };
 
     floatx4 acc[kWaveTiles][kWideSub], xacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -211,32 +237,27 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
         constexpr bool EXTRA = decltype(extra_c)::value;   // wave-uniform, fixed per workgroup
         const uint8_t *wst = wring + (o % kWRing) * kWStage;
         const uint8_t *mine = wst + wave * kWWave;
-        u32x4 code[kWaveTiles], xcode = {};
+        u32x4 code[kWaveTiles];
 #pragma unroll
         for (int tt = 0; tt < kWaveTiles; ++tt)
             code[tt] = *reinterpret_cast<const u32x4 *>(mine + tt * kCodeChunk + lane * 16);
         const uint32_t scl = *reinterpret_cast<const uint32_t *>(mine + kWaveTiles * kCodeChunk + lane * 4);
         const uint32_t sch = *reinterpret_cast<const uint32_t *>(mine + kWaveTiles * kCodeChunk + 256 + lane * 4);
-        uint32_t xs0 = 0, xs1 = 0;
-        if (EXTRA) {
-            xcode = *reinterpret_cast<const u32x4 *>(wst + kWXCode + lane * 16);
-            xs0 = *reinterpret_cast<const uint32_t *>(wst + kWXScale + c16 * 8);
-            xs1 = *reinterpret_cast<const uint32_t *>(wst + kWXScale + c16 * 8 + 4);
-        }
         uint32_t s0[4], s1[4];   // scale words (blocks 0..3, 4..7) of row r of each of the wave's tiles
         gather_lane_groups(scl, s0);
         gather_lane_groups(sch, s1);
         const uint8_t *xb = xs + (o % kXRing) * kXBuf;
+        const uint8_t *xab = xaring + (o % kXARing) * kXABuf + lane * 16;
         auto scale_of = [&](uint32_t w0, uint32_t w1, int d) {
             const int sh = 8 * ((2 * d + (g >> 1)) & 3);   // this lane's block of pair d
             return e4m3_f32<0>((d < 2 ? w0 : w1) >> sh);
         };
         auto decode = [&](int d, int tt) { return decode_scaled(code[tt][d], scale_of(s0[tt], s1[tt], d)); };
-        auto xdecode = [&](int d) { return decode_scaled(xcode[d], scale_of(xs0, xs1, d)); };
         auto read_b = [&](int d, int cs) {
             return *reinterpret_cast<const bf16x8 *>(xb + cs * 16 * kXColBytes + boff[d]);
         };
         auto read_xb = [&](int d) { return *reinterpret_cast<const bf16x8 *>(xb + xboff + boff[d]); };
+        auto read_xa = [&](int d) { return *reinterpret_cast<const bf16x8 *>(xab + d * kLanes * 16); };
         // Software pipeline over the four 32-k slices: a[d & 1] holds slice
         // d's A operands, slice d + 1's are decoded into the other half
         // between slice d's MFMAs, and each B operand is re-read for slice
@@ -248,12 +269,17 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
 #pragma unroll
         for (int tt = 0; tt < kWaveTiles; ++tt) a[0][tt] = decode(0, tt);
         if (EXTRA) {
-            xa[0] = xdecode(0);
+            xa[0] = read_xa(0);
             xbv = read_xb(0);
         }
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int cur = d & 1, nxt = cur ^ 1;
+            // Waves w and w + 4 share a SIMD; they take turns at the higher
+            // issue priority slice by slice, so neither runs a whole octet
+            // ahead and idles at the barrier while the other finishes alone.
+            if (((d + (wave >> 2)) & 1) != 0) __builtin_amdgcn_s_setprio(2);
+            else __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int cs = 0; cs < kWideSub; ++cs) {
 #pragma unroll
@@ -266,7 +292,7 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
                 xacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cur], xbv, xacc, 0, 0, 0);
                 if (d < 3) {
                     xbv = read_xb(d + 1);
-                    xa[nxt] = xdecode(d + 1);
+                    xa[nxt] = read_xa(d + 1);
                 }
             }
         }
@@ -276,26 +302,43 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
     // octet o a wave issues octet o + 1's X loads, then octet o + 2's weight
     // loads, so at the start of octet o + 1 only the latter may still be
     // outstanding: the wait below finishes this wave's loads of the octet
-    // about to be used, and the barrier publishes every wave's loads and
-    // frees the buffers restaged next (read at octet o - 1).  A bare
-    // barrier: __syncthreads() would also drain every outstanding load (its
-    // fence), emptying the rings; the memory clobber keeps the LDS reads
-    // below it.
+    // about to be used (and its LDS writes), and the barrier publishes every
+    // wave's loads and decoded extra operands and frees the buffers restaged
+    // next (read at octet o - 1).  A bare barrier: __syncthreads() would also
+    // drain every outstanding load (its fence), emptying the rings; the
+    // memory clobber keeps the LDS accesses on their side of it.  A decoder
+    // wave decodes octet o + 1's extra slice after octet o's MFMAs, once its
+    // own octet o + 1 weight loads (issued an octet earlier) are done.
     auto run = [&](auto extra_c) {
+        constexpr bool EXTRA = decltype(extra_c)::value;
+        const bool decoder = EXTRA && wave < kXDecoders;
         load_w(0);
         stage_x(0);
         if (octets > 1) load_w(1);
+        if (decoder) {
+            if (octets > 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+            asm volatile("" ::: "memory");   // the raw bytes' LDS reads stay below the wait
+            decode_extra(0);
+        }
         for (int o = 0; o < octets; ++o) {
-            if (o + 1 < octets) __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads));
+            if (o + 1 < octets) __builtin_amdgcn_s_waitcnt(vmcnt_lds(kWLoads));
             else __builtin_amdgcn_s_waitcnt(0);
             asm volatile("s_barrier" ::: "memory");
             if (o + 1 < octets) stage_x(o + 1);
             if (o + 2 < octets) load_w(o + 2);
             compute(o, extra_c);
+            if (decoder && o + 1 < octets) {
+                if (o + 2 < octets) __builtin_amdgcn_s_waitcnt(vmcnt_only(kXDmaPerWave + kWLoads));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_only(kXDmaPerWave));
+                asm volatile("" ::: "memory");
+                decode_extra(o + 1);
+            }
         }
     };
     if (has_extra) run(std::true_type{});
     else run(std::false_type{});
+    __builtin_amdgcn_s_setprio(0);
 
     // Lane (g, c16) holds rows 4g .. 4g + 3 of a tile for column
     // cs * 16 + c16 of the column tile.
