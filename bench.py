@@ -115,6 +115,17 @@ class Step:
                                   8 * mw.rows * mw.cols, "gemv"))
             self.launches.append((self._argmax(), gemv_bytes(head.rows, head.cols, 4) + 4 * 4,
                                   8 * head.rows * head.cols, "gemv"))
+        elif name == "draft_head_8192x4096":
+            m = w.matrices[0]
+            self.x = wl.activations(1, m.cols, seed=wl.seed_of(name, "x"), device=DEV)
+            self.mats = [Matrix(w, m, c) for c in range(w.copies)]
+            self.logits2 = [torch.empty(1, m.rows, dtype=torch.float32, device=DEV) for _ in range(2)]
+            self.am2 = [torch.empty(1, dtype=torch.int32, device=DEV) for _ in range(2)]
+            self.wsp = torch.empty(nv.nvfp4_gemv_argmax_workspace_bytes(m.rows, m.cols, 1), dtype=torch.uint8,
+                                   device=DEV)
+            for i, M in enumerate(self.mats):
+                self.launches.append((self._argmax_of(M, self.logits2[i % 2], self.am2[i % 2]),
+                                      gemv_bytes(M.rows, M.cols, 1) + 4, 2 * M.rows * M.cols, "gemv"))
         elif name == "prefill_n512":
             m = w.matrices[0]
             self.x = wl.activations(512, m.cols, seed=wl.seed_of(name, "x"), device=DEV)
@@ -150,6 +161,11 @@ class Step:
 
         def f():
             nv.nvfp4_gemv_argmax(M.wq, M.ws, M.tscale, M.rows, M.cols, self.x, 4, self.logits, self.am, self.wsp)
+        return f
+
+    def _argmax_of(self, M, logits, am):
+        def f():
+            nv.nvfp4_gemv_argmax(M.wq, M.ws, M.tscale, M.rows, M.cols, self.x, 1, logits, am, self.wsp)
         return f
 
     def run(self):
@@ -209,6 +225,9 @@ def cpu_baseline(step, budget_s=12.0):
         sample.append((step.M2, step.x, np.arange(0, step.M2.rows, 8)))
     elif w.name == "prefill_n512":
         sample.append((step.M, step.x, np.arange(0, step.M.rows, 256)))
+    elif w.name == "draft_head_8192x4096":
+        for M in step.mats:
+            sample.append((M, step.x, None))
     xb_cache = {}
     t_total, bytes_done, checked, worst = 0.0, 0, 0, 0.0
     for M, x, rows in sample:
@@ -318,7 +337,10 @@ def main():
     kernel = "gemm" if args.workload == "prefill_n512" else "gemv"
     n_launch = sum(1 for _, _, _, t in step.launches if t == kernel)
     per_launch_s = step_ev_s / n_launch
-    if tags == {kernel}:
+    if args.workload == "draft_head_8192x4096":
+        scope = ("average call: the product with per-workgroup argmax keys plus the one-workgroup argmax "
+                 "finish (HIP events around %d graph replays of %d calls)" % (args.steps, n_launch))
+    elif tags == {kernel}:
         scope = "average launch of the %s kernel (HIP events around %d graph replays of %d launches)" % (
             kernel, args.steps, n_launch)
     else:

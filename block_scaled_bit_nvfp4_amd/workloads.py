@@ -5,8 +5,10 @@ bf16 activations that both the HIP library and the CPU oracle consume (each
 side quantises and multiplies on its own).  Shapes stand in for the pages'
 workloads: single-stream decode of a 27B-class dense model (5120 hidden,
 17408 MLP width, a 151936-entry vocabulary), the K+1 = 4 column speculative
-verify, and a 512-token prefill chunk (bw24 README and wiki, performance and
-feature sections; qwentin README, "Performance" and "How it works").
+verify, a 512-token prefill chunk, and the trimmed-vocabulary draft head of
+speculative decoding (bw24 README and wiki, performance and feature
+sections, the FR-Spec draft trims; qwentin README, "Performance" and "How it
+works").
 
 Weights: fp32 N(0, 0.02); where a workload has outliers, every element is
 independently an outlier with probability 0.001 and is then replaced by
@@ -65,6 +67,13 @@ WORKLOADS = {
     "prefill_n512": Workload(
         "prefill_n512", "prefill-width contraction N=512: 17408x5120",
         512, (Matrix("w", 17408, 5120),), copies=1),
+    # A trimmed-vocabulary draft head (an 8192-row subset of a vocabulary at a
+    # 4096 hidden size: 18.9 MB at NVFP4) drafting one token per call;
+    # 16 copies (302 MB) rotate past the 256 MB Infinity Cache.
+    "draft_head_8192x4096": Workload(
+        "draft_head_8192x4096", "trimmed-vocabulary draft head 8192x4096 with argmax, N=1; "
+        "16 distinct heads rotated",
+        1, (Matrix("draft_head", 8192, 4096),), copies=16, argmax=("draft_head",)),
 }
 
 

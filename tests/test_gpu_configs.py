@@ -157,3 +157,23 @@ def test_prefill_n512_sampled():
     c_ref, s_ref = _oracle_rows(W, codes, scales, rows, w.tscale)
     Yr, S = oracle.gemv_rows(c_ref, s_ref, w.tscale, wl.bf16_bits(X))
     G.assert_within_tolerance(Y[:, rows], Yr, S, "prefill n512")
+
+
+def test_draft_head_8192x4096_full_argmax():
+    w = wl.WORKLOADS["draft_head_8192x4096"]
+    m = w.matrices[0]
+    X = wl.activations(1, m.cols, seed=wl.seed_of(w.name, "x"), device=G.DEV)
+    xb = wl.bf16_bits(X)
+    for copy in (0, w.copies - 1):
+        G.note("config draft_head_8192x4096 copy %d" % copy)
+        W, c, s, q, ss = _matrix(w, m, copy)
+        logits, am = G.gemv_argmax_gpu(q, ss, w.tscale, m.rows, m.cols, X)
+        c_ref, s_ref = oracle.quantize(W.cpu().numpy(), w.tscale)
+        assert np.array_equal(c.cpu().numpy(), c_ref)
+        assert np.array_equal(s.cpu().numpy(), s_ref)
+        Y, S = oracle.gemv(c_ref, s_ref, w.tscale, xb)
+        G.assert_within_tolerance(logits.cpu().numpy(), Y, S, "draft head logits")
+        assert list(am.cpu().numpy()) == list(oracle.argmax_first(Y))
+        # the argmax without stored logits names the same row
+        _, am2 = G.gemv_argmax_gpu(q, ss, w.tscale, m.rows, m.cols, X, with_logits=False)
+        assert torch.equal(am, am2)

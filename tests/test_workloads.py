@@ -7,7 +7,10 @@ from block_scaled_bit_nvfp4_amd import workloads as wl
 
 def test_workload_table():
     assert set(wl.WORKLOADS) == {"gemv_256x512", "decode_4096x4096", "mlp_27b_decode",
-                                 "verify_vocab_n4", "prefill_n512"}
+                                 "verify_vocab_n4", "prefill_n512", "draft_head_8192x4096"}
+    d = wl.WORKLOADS["draft_head_8192x4096"]
+    assert (d.matrices[0].rows, d.matrices[0].cols, d.n, d.copies) == (8192, 4096, 1, 16)
+    assert d.argmax == ("draft_head",)
     m = wl.WORKLOADS["mlp_27b_decode"].matrices
     assert (m[0].rows, m[0].cols, m[1].rows, m[1].cols) == (34816, 5120, 5120, 17408)
     assert wl.WORKLOADS["verify_vocab_n4"].n == 4
