@@ -14,6 +14,9 @@ consecutive elements of a row, one fp32 tensor scale; canonical layout
 ``codes[R][K/2]`` (element k in the low nibble of byte k/2 when k is even) and
 ``scales[R][K/16]``.
 
+A second block-scaled format, MXFP4 (E2M1 codes, one E8M0 power-of-two
+scale per 32 elements; ``mx_*`` functions), shares the E2M1 decode.
+
 Parity pins for every function here are in ``tests/test_oracle_*.py``.
 """
 from __future__ import annotations
@@ -84,6 +87,17 @@ def _load():
         lib.oracle_swiglu.argtypes = [P, i64, i64, P]
         lib.oracle_repack.restype = None
         lib.oracle_repack.argtypes = [P, P, i64, i64, P, P]
+        lib.oracle_e8m0_value.restype = ctypes.c_double
+        lib.oracle_e8m0_value.argtypes = [ctypes.c_int]
+        lib.oracle_mx_quantize.restype = None
+        lib.oracle_mx_quantize.argtypes = [P, i64, i64, ctypes.c_float, P, P]
+        lib.oracle_mx_dequant.restype = None
+        lib.oracle_mx_dequant.argtypes = [P, P, ctypes.c_float, i64, i64, P]
+        lib.oracle_mx_gemv_rows.restype = None
+        lib.oracle_mx_gemv_rows.argtypes = [P, P, ctypes.c_float, i64, i64, P, i64,
+                                            P, i64, P, P]
+        lib.oracle_mx_repack.restype = None
+        lib.oracle_mx_repack.argtypes = [P, P, i64, i64, P, P]
         _lib = lib
         return lib
 
@@ -245,4 +259,82 @@ def repack(codes, scales):
     wq = np.empty(ST * O * 4 * 64 * 16, np.uint8)
     ws = np.empty(ST * O * 4 * 16 * 8, np.uint8)
     _load().oracle_repack(_ptr(codes), _ptr(scales), R, K, _ptr(wq), _ptr(ws))
+    return wq, ws
+
+
+# -------------------------------------------------------------------- MXFP4 --
+# The second block-scaled format (see the MXFP4 part of nvfp4_oracle.c): E2M1
+# codes, one E8M0 scale byte (2^(b - 127)) per 32 elements of a row, an fp32
+# tensor multiplier; canonical codes [R][K/2], scales [R][K/32].
+
+def _check_mx_shape(R: int, K: int):
+    if R < 0 or K <= 0 or K % 32:
+        raise ValueError("need R >= 0 and K a positive multiple of 32, got %d x %d" % (R, K))
+
+
+def e8m0_value(byte: int) -> float:
+    return _load().oracle_e8m0_value(int(byte))
+
+
+def mx_quantize(W: np.ndarray, tscale: float = 1.0):
+    """fp32 W[R][K] -> (codes uint8 [R][K/2], scales uint8 [R][K/32])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    R, K = W.shape
+    _check_mx_shape(R, K)
+    codes = np.zeros((R, K // 2), np.uint8)
+    scales = np.zeros((R, K // 32), np.uint8)
+    _load().oracle_mx_quantize(_ptr(W), R, K, float(tscale), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def mx_dequant(codes: np.ndarray, scales: np.ndarray, tscale: float = 1.0) -> np.ndarray:
+    """Exact fp64 w_hat[R][K] = e2m1 * e8m0 * tscale."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    R, K = codes.shape[0], codes.shape[1] * 2
+    _check_mx_shape(R, K)
+    assert scales.shape == (R, K // 32)
+    out = np.empty((R, K), np.float64)
+    _load().oracle_mx_dequant(_ptr(codes), _ptr(scales), float(tscale), R, K, _ptr(out))
+    return out
+
+
+def mx_gemv_rows(codes, scales, tscale: float, X_bits: np.ndarray, rows=None):
+    """As gemv_rows, for MXFP4 weights."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    R, K = codes.shape[0], codes.shape[1] * 2
+    _check_mx_shape(R, K)
+    assert scales.shape == (R, K // 32)
+    X_bits = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    if X_bits.ndim == 1:
+        X_bits = X_bits[None, :]
+    N = X_bits.shape[0]
+    assert X_bits.shape[1] == K
+    if rows is None:
+        rows = np.arange(R, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < R)
+    Y = np.zeros((N, rows.size), np.float64)
+    S = np.zeros((N, rows.size), np.float64)
+    _load().oracle_mx_gemv_rows(_ptr(codes), _ptr(scales), float(tscale), R, K,
+                                _ptr(X_bits), N, _ptr(rows), rows.size, _ptr(Y), _ptr(S))
+    return Y, S
+
+
+def mx_gemv(codes, scales, tscale: float, X_bits: np.ndarray):
+    return mx_gemv_rows(codes, scales, tscale, X_bits, None)
+
+
+def mx_repack(codes, scales):
+    """Canonical MXFP4 (codes, scales) -> repacked (code plane, scale plane) bytes."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    R, K = codes.shape[0], codes.shape[1] * 2
+    _check_mx_shape(R, K)
+    ST = ((R + 15) // 16 + 3) // 4
+    O = (K + 127) // 128
+    wq = np.empty(ST * O * 4 * 64 * 16, np.uint8)
+    ws = np.empty(ST * O * 4 * 16 * 4, np.uint8)
+    _load().oracle_mx_repack(_ptr(codes), _ptr(scales), R, K, _ptr(wq), _ptr(ws))
     return wq, ws

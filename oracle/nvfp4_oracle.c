@@ -308,3 +308,152 @@ void oracle_repack(const uint8_t *codes, const uint8_t *scales, int64_t R, int64
         }
     }
 }
+
+/* ============================================================== MXFP4 -- */
+/*
+ * The second block-scaled format on the same skeleton: E2M1 element codes
+ * with one power-of-two scale per 32 consecutive elements of a row, the
+ * "E8M0-style" scale the pages set beside NVFP4 (bw24 wiki, feature list:
+ * the E2M1 weight class; qwentin README, "Why it's interesting").  The
+ * pages do not define it; the plainest reading is the OCP Microscaling (MX)
+ * MXFP4 format, which this part implements:
+ *   element  E2M1 code, as above;
+ *   scale    E8M0 byte b: 2^(b - 127); b = 0xFF is NaN; no sign, no zero;
+ *   block    32 consecutive elements of a row; canonical layout
+ *            codes [R][K/2] (nibble order as NVFP4), scales [R][K/32];
+ *   tensor   one fp32 multiplier, as for NVFP4 (1.0 in every workload).
+ */
+
+/* E8M0 byte -> exact value 2^(b - 127); 0xFF is NaN. */
+double oracle_e8m0_value(int byte)
+{
+    if ((byte & 0xFF) == 0xFF)
+        return NAN;
+    return ldexp(1.0, (byte & 0xFF) - 127);
+}
+
+/* Quantise an fp32 matrix W[R][K] (row-major, K % 32 == 0) to MXFP4 in the
+ * canonical layout.  Per 32-element block of a row, following the MX
+ * definition's conversion of a vector to one shared scale:
+ *   q = amax / tscale;  E = floor(log2 q) - 2  (2 = the largest exponent of
+ *   an E2M1 value, 6 = 1.5 * 2^2), clamped to [-127, 127]; q = 0 gives
+ *   E = -127;  scale byte = E + 127;
+ *   code_i = sign(w_i) | E2M1_RNE(|w_i| / (2^E * tscale))  (ties to even,
+ *   saturating at 6: a block's largest element lies in [4, 8) * 2^E, so
+ *   values above 6 * 2^E clip to 6).
+ * floor(log2 q) is read exactly off the fp64 exponent of q (frexp); q is a
+ * quotient of two fp32 values, so it is exactly a power of two or at least
+ * 2^-24 relatively away from one, and fp64 keeps that side.  The element
+ * quotient is decided as in oracle_quantize. */
+void oracle_mx_quantize(const float *W, int64_t R, int64_t K, float tscale,
+                        uint8_t *codes, uint8_t *scales)
+{
+    int64_t KB = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t b = 0; b < KB; ++b) {
+            const float *w = W + r * K + b * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                double a = fabs((double)w[i]);
+                if (a > amax) amax = a;
+            }
+            double q = amax / (double)tscale;
+            int E;
+            if (q > 0.0) {
+                int e;
+                frexp(q, &e);            /* q = f * 2^e, f in [0.5, 1): floor(log2 q) = e - 1 */
+                E = (e - 1) - 2;
+                if (E < -127) E = -127;
+                if (E > 127) E = 127;
+            } else {
+                E = -127;
+            }
+            scales[r * KB + b] = (uint8_t)(E + 127);
+            double denom = ldexp(1.0, E) * (double)tscale;
+            for (int i = 0; i < 32; i += 2) {
+                int c[2];
+                for (int h = 0; h < 2; ++h) {
+                    double v = fabs((double)w[i + h]) / denom;
+                    c[h] = oracle_e2m1_encode_mag(v) | (signbit(w[i + h]) ? 8 : 0);
+                }
+                codes[r * (K / 2) + b * 16 + i / 2] = (uint8_t)(c[0] | (c[1] << 4));
+            }
+        }
+    }
+}
+
+/* Exact dequantised MXFP4 element (r, k): e2m1(code) * e8m0(scale) * tscale. */
+static double mx_w_hat(const uint8_t *codes, const uint8_t *scales, float tscale,
+                       int64_t K, int64_t r, int64_t k)
+{
+    uint8_t byte = codes[r * (K / 2) + k / 2];
+    int code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+    return oracle_e2m1_value(code) * oracle_e8m0_value(scales[r * (K / 32) + k / 32])
+           * (double)tscale;
+}
+
+void oracle_mx_dequant(const uint8_t *codes, const uint8_t *scales, float tscale,
+                       int64_t R, int64_t K, double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t k = 0; k < K; ++k)
+            out[r * K + k] = mx_w_hat(codes, scales, tscale, K, r, k);
+}
+
+/* As oracle_gemv_rows, for MXFP4 weights. */
+void oracle_mx_gemv_rows(const uint8_t *codes, const uint8_t *scales, float tscale,
+                         int64_t R, int64_t K, const uint16_t *X, int64_t N,
+                         const int64_t *rows, int64_t nrows, double *Y, double *S)
+{
+    (void)R;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < nrows; ++i) {
+        int64_t r = rows[i];
+        for (int64_t n = 0; n < N; ++n) {
+            double y = 0.0, s = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = mx_w_hat(codes, scales, tscale, K, r, k)
+                           * oracle_bf16_value(X[n * K + k]);
+                y += p;
+                s += fabs(p);
+            }
+            Y[n * nrows + i] = y;
+            if (S) S[n * nrows + i] = s;
+        }
+    }
+}
+
+/* Reference of the library's MXFP4 repacked layout, from its published
+ * definition: the code plane is the NVFP4 code plane of the same codes
+ * (tiles of 16 rows, super-tiles of 4 tiles, octets of 128 elements; entry
+ * (st, o, tt, l = 16g + r) bytes 4d..4d+3 hold elements
+ * 32(4o + d) + 8g .. +7 of row 64st + 16tt + r, i.e. the code bytes
+ * 16(4o + d) + 4g .. +3 of that row); the scale plane is
+ * [ST][O][4][16][4 bytes]: entry (st, o, tt, r) byte i is the scale of
+ * 32-element block 4o + i of that row; O = ceil(K / 128); positions past
+ * the last row or block hold 0. */
+void oracle_mx_repack(const uint8_t *codes, const uint8_t *scales, int64_t R, int64_t K,
+                      uint8_t *wq, uint8_t *ws)
+{
+    int64_t KB = K / 32;
+    int64_t T = (R + 15) / 16;
+    int64_t ST = (T + 3) / 4;
+    int64_t O = (K + 127) / 128;
+    memset(wq, 0, (size_t)(ST * O * 4 * 64 * 16));
+    memset(ws, 0, (size_t)(ST * O * 4 * 16 * 4));
+    for (int64_t row = 0; row < R; ++row) {
+        int64_t st = row / 64, tt = (row % 64) / 16, r = row % 16;
+        for (int64_t j = 0; j < K / 32; ++j) {          /* 32-element slice */
+            int64_t o = j / 4, d = j % 4;
+            for (int64_t g = 0; g < 4; ++g) {
+                int64_t l = 16 * g + r;
+                uint8_t *dst = wq + (((st * O + o) * 4 + tt) * 64 + l) * 16 + 4 * d;
+                memcpy(dst, codes + row * (K / 2) + 16 * j + 4 * g, 4);
+            }
+        }
+        for (int64_t b = 0; b < KB; ++b)
+            ws[(((st * O + b / 4) * 4 + tt) * 16 + r) * 4 + b % 4] = scales[row * KB + b];
+    }
+}
