@@ -21,7 +21,9 @@ __all__ = [
     "nvfp4_quantize", "nvfp4_repack", "nvfp4_dequant", "nvfp4_gemv",
     "nvfp4_gemv_argmax_workspace_bytes", "nvfp4_gemv_argmax", "nvfp4_swiglu",
     "nvfp4_gemv_swiglu",
-    "alloc_repacked",
+    "mxfp4_repacked_code_bytes", "mxfp4_repacked_scale_bytes", "mxfp4_quantize", "mxfp4_repack",
+    "mxfp4_dequant", "mxfp4_gemv",
+    "alloc_repacked", "alloc_mx_repacked",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +68,12 @@ def load():
             "nvfp4_gemv_argmax": (i32, [P, P, f32, i64, i64, P, i32, P, P, P, sz, P]),
             "nvfp4_swiglu": (i32, [P, i64, i32, P, P]),
             "nvfp4_gemv_swiglu": (i32, [P, P, f32, i64, i64, P, i32, P, P, P]),
+            "mxfp4_repacked_code_bytes": (sz, [i64, i64]),
+            "mxfp4_repacked_scale_bytes": (sz, [i64, i64]),
+            "mxfp4_quantize": (i32, [P, i64, i64, f32, P, P, P]),
+            "mxfp4_repack": (i32, [P, P, i64, i64, P, P, P]),
+            "mxfp4_dequant": (i32, [P, P, f32, i64, i64, P, P, P]),
+            "mxfp4_gemv": (i32, [P, P, f32, i64, i64, P, i32, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(lib, name)
@@ -156,5 +164,44 @@ def alloc_repacked(rows: int, cols: int, device="cuda"):
     nq, ns = nvfp4_repacked_code_bytes(rows, cols), nvfp4_repacked_scale_bytes(rows, cols)
     if nq == 0:
         raise NVFP4Error(-2, "alloc_repacked")
+    return (torch.empty(nq, dtype=torch.uint8, device=device),
+            torch.empty(ns, dtype=torch.uint8, device=device))
+
+
+# ------------------------------------------------------------------- MXFP4 --
+
+def mxfp4_repacked_code_bytes(rows: int, cols: int) -> int:
+    return int(load().mxfp4_repacked_code_bytes(rows, cols))
+
+
+def mxfp4_repacked_scale_bytes(rows: int, cols: int) -> int:
+    return int(load().mxfp4_repacked_scale_bytes(rows, cols))
+
+
+def mxfp4_quantize(W, rows, cols, tscale, codes, scales, stream=None):
+    _check(load().mxfp4_quantize(_ptr(W), rows, cols, float(tscale), _ptr(codes), _ptr(scales),
+                                 _stream(stream, W)), "mxfp4_quantize")
+
+
+def mxfp4_repack(codes, scales, rows, cols, wq, ws, stream=None):
+    _check(load().mxfp4_repack(_ptr(codes), _ptr(scales), rows, cols, _ptr(wq), _ptr(ws),
+                               _stream(stream, codes)), "mxfp4_repack")
+
+
+def mxfp4_dequant(wq, ws, tscale, rows, cols, out_f32=None, out_bf16=None, stream=None):
+    _check(load().mxfp4_dequant(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(out_f32),
+                                _ptr(out_bf16), _stream(stream, wq)), "mxfp4_dequant")
+
+
+def mxfp4_gemv(wq, ws, tscale, rows, cols, X, n, Y, stream=None):
+    _check(load().mxfp4_gemv(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(X), int(n), _ptr(Y),
+                             _stream(stream, wq)), "mxfp4_gemv")
+
+
+def alloc_mx_repacked(rows: int, cols: int, device="cuda"):
+    """Allocate (uninitialised) MXFP4 code and scale planes for mxfp4_repack."""
+    nq, ns = mxfp4_repacked_code_bytes(rows, cols), mxfp4_repacked_scale_bytes(rows, cols)
+    if nq == 0:
+        raise NVFP4Error(-2, "alloc_mx_repacked")
     return (torch.empty(nq, dtype=torch.uint8, device=device),
             torch.empty(ns, dtype=torch.uint8, device=device))

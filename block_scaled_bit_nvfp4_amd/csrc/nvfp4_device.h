@@ -25,6 +25,14 @@ constexpr int kScaleChunk = kTileRows * kOctet;       // one tile's octet of sca
 constexpr int kCodeRegion = kSuperTiles * kCodeChunk;     // one super-tile's octet: 4 KiB
 constexpr int kScaleRegion = kSuperTiles * kScaleChunk;   // 512 B
 
+// The second block-scaled format, MXFP4: the same E2M1 codes and code plane,
+// one E8M0 scale byte (2^(b - 127)) per 32 elements; its scale plane holds
+// 4 bytes per row and octet (the octet's four 32-element blocks).
+enum ScaleFormat { kNvfp4 = 0, kMxfp4 = 1 };
+constexpr int kMxBlock = 32;
+constexpr int kMxScaleChunk = kTileRows * 4;                 // one tile's octet of MX scales: 64 B
+constexpr int kMxScaleRegion = kSuperTiles * kMxScaleChunk;  // 256 B
+
 typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -72,6 +80,29 @@ __device__ __forceinline__ float e4m3_f32_dyn(uint32_t word, int byte) {
         case 2: return e4m3_f32<2>(word);
         default: return e4m3_f32<3>(word);
     }
+}
+
+// E8M0 byte b -> fp32 2^(b - 127): b = 0 is the subnormal 2^-127, 0xFF NaN.
+__device__ __forceinline__ float e8m0_f32(uint32_t b) {
+    b &= 0xFFu;
+    return __uint_as_float(b == 0xFFu ? 0x7FC00000u : (b == 0u ? 0x00400000u : b << 23));
+}
+
+// Eight E2M1 codes (one word) times 2^(b - 127) -> the eight exact bf16
+// values of an MFMA operand.  The scaled conversion multiplies by the power
+// of two in its scale operand's exponent field, so the E8M0 byte goes there
+// (b = 0 gives 2^-127 as well); every product e2m1 * 2^(b - 127) below
+// bf16's overflow is a bf16 value.  For finite bytes (not 0xFF).
+__device__ __forceinline__ bf16x8 e2m1x8_bf16_e8m0(uint32_t word, uint32_t b) {
+    const float s = __uint_as_float((b & 0xFFu) << 23);
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 3);
+    bf16x8 o;
+    o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1];
+    o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
+    return o;
 }
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }

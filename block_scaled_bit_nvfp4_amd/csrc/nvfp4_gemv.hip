@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(256) swiglu_kernel(const float *__restrict__ g
 //   g, u = tscale * sum, and Y (when not NULL) receives g and u at the stacked
 //   positions, so every bit equals the plain product followed by the SwiGLU
 //   kernel.
-template <int N, int TWW, int MODE>
+template <int N, int TWW, int MODE, int FMT = kNvfp4>
 __global__ void __launch_bounds__(kLanes * kMaxKsplit)
 narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows, int octets,
               int kb, int ksplit, const uint16_t *__restrict__ X, int K, float *__restrict__ Y,
@@ -73,8 +73,8 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
     float *const red = reinterpret_cast<float *>(lds + int(blockDim.x >> 6) * WL);
 
     float acc[TWW][H];
-    narrow_accumulate<N, TWW>(wq, ws, int64_t(st) + (half ? up_st : 0), tg, o0, o1, octets, kb, X, K, lane, acc,
-                              lds + wave * WL);
+    narrow_accumulate<N, TWW, FMT>(wq, ws, int64_t(st) + (half ? up_st : 0), tg, o0, o1, octets, kb, X, K, lane,
+                                   acc, lds + wave * WL);
     {
         const int g = lane >> 4, r = lane & 15;
 #pragma unroll
@@ -183,7 +183,7 @@ argmax_finish_kernel(const unsigned long long *__restrict__ keys, int groups, in
 
 // ------------------------------------------------------------------ dispatch
 
-template <int MODE, int TWW>
+template <int MODE, int TWW, int FMT = kNvfp4>
 int launch_narrow_tww(const Geometry &g, const NarrowConfig &cfg, const uint8_t *wq, const uint8_t *ws,
                       float tscale, const uint16_t *X, int n, float *Y, unsigned long long *amax_ws,
                       int32_t *argmax_out, int up_st, uint16_t *h, int waves, int64_t groups, hipStream_t stream) {
@@ -191,7 +191,7 @@ int launch_narrow_tww(const Geometry &g, const NarrowConfig &cfg, const uint8_t 
     const size_t lds = size_t(waves) * (size_t(narrow_wave_lds_bytes(n)) + size_t(n) * TWW * kTileRows * sizeof(float));
     const int rows = int(g.rows), octets = int(g.octets), kb = int(g.kb), K = int(g.cols);
 #define NVFP4_LAUNCH(NN)                                                                                      \
-    hipLaunchKernelGGL((narrow_kernel<NN, TWW, MODE>), grid, block, lds, stream, wq, ws, tscale, rows, octets, \
+    hipLaunchKernelGGL((narrow_kernel<NN, TWW, MODE, FMT>), grid, block, lds, stream, wq, ws, tscale, rows, octets, \
                        kb, cfg.ksplit, X, K, Y, amax_ws, argmax_out, up_st, h)
     switch (n) {
         case 1: NVFP4_LAUNCH(1); break;
@@ -223,7 +223,21 @@ int launch_narrow(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float
 }
 
 int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
-                int n, float *Y, hipStream_t stream);
+                int n, float *Y, hipStream_t stream, int fmt = kNvfp4);
+
+// The MXFP4 matvec: the plain product's decomposition and kernel with the
+// E8M0 scale plane (the tile rule never picks four tiles per workgroup).
+int launch_narrow_mx(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
+                     int n, float *Y, hipStream_t stream) {
+    const NarrowConfig cfg = narrow_config(g);
+    switch (cfg.tww) {
+        case 1: return launch_narrow_tww<kPlain, 1, kMxfp4>(g, cfg, wq, ws, tscale, X, n, Y, nullptr, nullptr, 0,
+                                                            nullptr, cfg.ksplit, cfg.groups, stream);
+        case 2: return launch_narrow_tww<kPlain, 2, kMxfp4>(g, cfg, wq, ws, tscale, X, n, Y, nullptr, nullptr, 0,
+                                                            nullptr, cfg.ksplit, cfg.groups, stream);
+        default: return NVFP4_EINVAL;
+    }
+}
 
 // True when the fused gate||up+SwiGLU kernel reproduces the stacked product's
 // decomposition: the up rows start on a super-tile boundary and a workgroup
@@ -337,4 +351,18 @@ NVFP4_API int nvfp4_swiglu(const float *gu, int64_t F, int n, uint16_t *h, hipSt
     (void)hipGetLastError();
     hipLaunchKernelGGL(swiglu_kernel, dim3(unsigned(ceil_div(total, 256))), dim3(256), 0, stream, gu, F, total, h);
     return launch_status();
+}
+
+// ------------------------------------------------------------------ MXFP4
+
+NVFP4_API int mxfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
+                         const uint16_t *X, int n, float *Y, hipStream_t stream) {
+    if (!Y) return NVFP4_EINVAL;
+    if (int st = check_product_args(wq, ws, tscale, rows, cols, X, n)) return st;
+    if (int st = check_mx_shape(rows, cols)) return st;
+    if (!aligned(Y, 4)) return NVFP4_EALIGN;
+    const Geometry g(rows, cols);
+    (void)hipGetLastError();
+    if (n <= kMaxNarrowN) return launch_narrow_mx(g, wq, ws, tscale, X, n, Y, stream);
+    return launch_mfma(g, wq, ws, tscale, X, n, Y, stream, kMxfp4);
 }

@@ -23,6 +23,12 @@ inline int check_shape(int64_t rows, int64_t cols) {
     return NVFP4_OK;
 }
 
+// MXFP4 takes whole 32-element blocks.
+inline int check_mx_shape(int64_t rows, int64_t cols) {
+    if (int st = check_shape(rows, cols)) return st;
+    return cols % kMxBlock == 0 ? NVFP4_OK : NVFP4_ESHAPE;
+}
+
 inline bool tscale_ok(float t) { return t > 0.0f && t <= 3.4028234663852886e38f; }
 
 struct Geometry {
@@ -36,6 +42,8 @@ struct Geometry {
           supertiles(ceil_div(ceil_div(r, kTileRows), kSuperTiles)), octets(ceil_div(c / kBlock, kOctet)) {}
     size_t code_bytes() const { return size_t(supertiles) * size_t(octets) * kCodeRegion; }
     size_t scale_bytes() const { return size_t(supertiles) * size_t(octets) * kScaleRegion; }
+    size_t mx_scale_bytes() const { return size_t(supertiles) * size_t(octets) * kMxScaleRegion; }
+    size_t scale_bytes(int fmt) const { return fmt == kMxfp4 ? mx_scale_bytes() : scale_bytes(); }
 };
 
 inline int launch_status() {

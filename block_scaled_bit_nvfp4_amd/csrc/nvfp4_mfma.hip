@@ -122,10 +122,14 @@ struct WideConfig {
     int64_t groups;   // launched workgroups (whole XCD rounds; the excess leaves at once)
 };
 
-__global__ void __launch_bounds__(kWideWaves * kLanes, 2)
-wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows, int supertiles,
-            int octets, int K, const uint16_t *__restrict__ X, int n, float *__restrict__ Y, int row_groups,
-            int col_groups, int extra, int vec_store) {
+// FMT kMxfp4: the scale plane holds a row's four E8M0 bytes per octet, and
+// word d of a code entry (32-element block d of the octet) is decoded by the
+// scaled conversion alone (the power of two goes into its scale operand).
+template <int FMT>
+__device__ __forceinline__ void
+wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows, int supertiles,
+          int octets, int K, const uint16_t *__restrict__ X, int n, float *__restrict__ Y, int row_groups,
+          int col_groups, int extra, int vec_store) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // X ring, then the weight ring
     asm volatile("" ::: "a0");   // lets the accumulators live in AGPRs
 
@@ -147,19 +151,21 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
     const int unit = rg * kWideSupers + (wave >> 1);
     const int half = wave & 1;
     const bool has_unit = unit < supertiles;
+    constexpr int SREGION = FMT == kMxfp4 ? kMxScaleRegion : kScaleRegion;
+    constexpr int SCHUNK = FMT == kMxfp4 ? kMxScaleChunk : kScaleChunk;
     const int64_t ubase = int64_t(has_unit ? unit : 0) * octets;
     const auto crs = make_rsrc(wq + ubase * kCodeRegion + half * kWaveTiles * kCodeChunk,
                                has_unit ? uint32_t(octets) * kCodeRegion : 0u);
-    const auto srs = make_rsrc(ws + ubase * kScaleRegion + half * kWaveTiles * kScaleChunk,
-                               has_unit ? uint32_t(octets) * kScaleRegion : 0u);
+    const auto srs = make_rsrc(ws + ubase * SREGION + half * kWaveTiles * SCHUNK,
+                               has_unit ? uint32_t(octets) * SREGION : 0u);
     // The extra tile of this workgroup (each wave takes column subtile wave).
     const int xtile = row_groups * kWideSupers * kSuperTiles + rg;
     const bool has_extra = rg < extra && xtile < supertiles * kSuperTiles;
     const int64_t xbase = has_extra ? int64_t(xtile >> 2) * octets : 0;
     const auto xcrs = make_rsrc(wq + xbase * kCodeRegion + (xtile & 3) * kCodeChunk,
                                 has_extra ? uint32_t(octets) * kCodeRegion : 0u);
-    const auto xsrs = make_rsrc(ws + xbase * kScaleRegion + (xtile & 3) * kScaleChunk,
-                                has_extra ? uint32_t(octets) * kScaleRegion : 0u);
+    const auto xsrs = make_rsrc(ws + xbase * SREGION + (xtile & 3) * SCHUNK,
+                                has_extra ? uint32_t(octets) * SREGION : 0u);
     // This workgroup's columns of X; columns past n read zeros.
     const int ncols = n - n0 < kWideCols ? n - n0 : kWideCols;
     const auto xrs = make_rsrc(X + int64_t(n0) * K, uint32_t(ncols) * uint32_t(K) * 2u);
@@ -192,13 +198,23 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
         for (int j = 0; j < kWaveTiles; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, lds_ptr(mine + j * kCodeChunk), 16, co + j * kCodeChunk, 0, 0,
                                                      kStream);
-        const uint32_t so = lane < 32 ? uint32_t(o) * kScaleRegion + uint32_t(lane) * 8u : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk), 4, so, 0, 0, kStream);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk + 256), 4,
-                                                 so == kOutOfRange ? so : so + 4, 0, 0, kStream);
+        if constexpr (FMT == kMxfp4) {
+            // one dword per row (lane 16 j + r: row r of tile j), and a
+            // placeholder load for an equal count
+            const uint32_t so = lane < 32 ? uint32_t(o) * SREGION + uint32_t(lane) * 4u : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk), 4, so, 0, 0, kStream);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(dst + kWDummy), 4, kOutOfRange, 0, 0, kStream);
+        } else {
+            const uint32_t so = lane < 32 ? uint32_t(o) * SREGION + uint32_t(lane) * 8u : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk), 4, so, 0, 0, kStream);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk + 256), 4,
+                                                     so == kOutOfRange ? so : so + 4, 0, 0, kStream);
+        }
         if (wave < kXDecoders) {
             uint8_t *xw = dst + kWXCode + wave * kWXWave;
-            const uint32_t xso = lane < 32 ? uint32_t(o) * kScaleRegion + uint32_t(lane) * 4u : kOutOfRange;
+            // the extra tile's 16 rows of scale bytes: 8 per row (NVFP4) or 4 (MXFP4)
+            const int xlanes = FMT == kMxfp4 ? 16 : 32;
+            const uint32_t xso = lane < xlanes ? uint32_t(o) * SREGION + uint32_t(lane) * 4u : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xcrs, lds_ptr(xw), 16, co, 0, 0, kStream);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(xw + kCodeChunk), 4, xso, 0, 0, kStream);
         } else {
@@ -214,10 +230,15 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
         const uint8_t *xw = wring + (o % kWRing) * kWStage + kWXCode + wave * kWXWave;
         const int d = wave;
         const uint32_t word = *reinterpret_cast<const uint32_t *>(xw + lane * 16 + d * 4);
-        const uint32_t sw = *reinterpret_cast<const uint32_t *>(xw + kCodeChunk + c16 * 8 + (d < 2 ? 0 : 4));
-        const float sc = e4m3_f32<0>(sw >> (8 * ((2 * d + (g >> 1)) & 3)));
-        *reinterpret_cast<bf16x8 *>(xaring + (o % kXARing) * kXABuf + d * kLanes * 16 + lane * 16) =
-            decode_scaled(word, sc);
+        bf16x8 v;
+        if constexpr (FMT == kMxfp4) {
+            const uint32_t sw = *reinterpret_cast<const uint32_t *>(xw + kCodeChunk + c16 * 4);
+            v = e2m1x8_bf16_e8m0(word, sw >> (8 * d));
+        } else {
+            const uint32_t sw = *reinterpret_cast<const uint32_t *>(xw + kCodeChunk + c16 * 8 + (d < 2 ? 0 : 4));
+            v = decode_scaled(word, e4m3_f32<0>(sw >> (8 * ((2 * d + (g >> 1)) & 3))));
+        }
+        *reinterpret_cast<bf16x8 *>(xaring + (o % kXARing) * kXABuf + d * kLanes * 16 + lane * 16) = v;
     };
 
     floatx4 acc[kWaveTiles][kWideSub], xacc = {0.f, 0.f, 0.f, 0.f};
@@ -242,17 +263,22 @@ wide_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, floa
         for (int tt = 0; tt < kWaveTiles; ++tt)
             code[tt] = *reinterpret_cast<const u32x4 *>(mine + tt * kCodeChunk + lane * 16);
         const uint32_t scl = *reinterpret_cast<const uint32_t *>(mine + kWaveTiles * kCodeChunk + lane * 4);
-        const uint32_t sch = *reinterpret_cast<const uint32_t *>(mine + kWaveTiles * kCodeChunk + 256 + lane * 4);
-        uint32_t s0[4], s1[4];   // scale words (blocks 0..3, 4..7) of row r of each of the wave's tiles
+        uint32_t s0[4], s1[4] = {0u, 0u, 0u, 0u};   // scale words (blocks 0..3, 4..7) of row r of each tile
         gather_lane_groups(scl, s0);
-        gather_lane_groups(sch, s1);
+        if constexpr (FMT != kMxfp4) {
+            const uint32_t sch = *reinterpret_cast<const uint32_t *>(mine + kWaveTiles * kCodeChunk + 256 + lane * 4);
+            gather_lane_groups(sch, s1);
+        }
         const uint8_t *xb = xs + (o % kXRing) * kXBuf;
         const uint8_t *xab = xaring + (o % kXARing) * kXABuf + lane * 16;
         auto scale_of = [&](uint32_t w0, uint32_t w1, int d) {
             const int sh = 8 * ((2 * d + (g >> 1)) & 3);   // this lane's block of pair d
             return e4m3_f32<0>((d < 2 ? w0 : w1) >> sh);
         };
-        auto decode = [&](int d, int tt) { return decode_scaled(code[tt][d], scale_of(s0[tt], s1[tt], d)); };
+        auto decode = [&](int d, int tt) {
+            if constexpr (FMT == kMxfp4) return e2m1x8_bf16_e8m0(code[tt][d], s0[tt] >> (8 * d));
+            else return decode_scaled(code[tt][d], scale_of(s0[tt], s1[tt], d));
+        };
         auto read_b = [&](int d, int cs) {
             return *reinterpret_cast<const bf16x8 *>(xb + cs * 16 * kXColBytes + boff[d]);
         };
@@ -389,22 +415,44 @@ inline WideConfig wide_config(const Geometry &g, int n, int cus) {
     return c;
 }
 
+// The two formats' kernels.
+__global__ void __launch_bounds__(kWideWaves * kLanes, 2)
+wide_kernel_nvfp4(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows,
+                  int supertiles, int octets, int K, const uint16_t *__restrict__ X, int n, float *__restrict__ Y,
+                  int row_groups, int col_groups, int extra, int vec_store) {
+    wide_body<kNvfp4>(wq, ws, tscale, rows, supertiles, octets, K, X, n, Y, row_groups, col_groups, extra, vec_store);
+}
+
+__global__ void __launch_bounds__(kWideWaves * kLanes, 2)
+wide_kernel_mxfp4(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows,
+                  int supertiles, int octets, int K, const uint16_t *__restrict__ X, int n, float *__restrict__ Y,
+                  int row_groups, int col_groups, int extra, int vec_store) {
+    wide_body<kMxfp4>(wq, ws, tscale, rows, supertiles, octets, K, X, n, Y, row_groups, col_groups, extra, vec_store);
+}
+
 int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
-                int n, float *Y, hipStream_t stream) {
-    if (g.cols > kMaxWideCols || int64_t(g.scale_bytes()) > kMaxWideScaleBytes) return NVFP4_ESHAPE;
+                int n, float *Y, hipStream_t stream, int fmt) {
+    if (g.cols > kMaxWideCols || int64_t(g.scale_bytes(fmt)) > kMaxWideScaleBytes) return NVFP4_ESHAPE;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 0;
     const WideConfig c = wide_config(g, n, cus);
     if (c.groups > (int64_t(1) << 31) - 1) return NVFP4_ESHAPE;
-    // The rings (136 KiB) are above the default dynamic-LDS limit.
-    if (hipFuncSetAttribute(reinterpret_cast<const void *>(wide_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kWideLds) != hipSuccess)
+    // The rings (148 KiB) are above the default dynamic-LDS limit.
+    const void *kern = fmt == kMxfp4 ? reinterpret_cast<const void *>(wide_kernel_mxfp4)
+                                     : reinterpret_cast<const void *>(wide_kernel_nvfp4);
+    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds) != hipSuccess)
         return NVFP4_EHIP;
-    hipLaunchKernelGGL(wide_kernel, dim3(unsigned(c.groups)), dim3(kWideWaves * kLanes), kWideLds, stream, wq,
-                       ws, tscale, int(g.rows), int(g.supertiles), int(g.octets), int(g.cols), X, n, Y, c.row_groups,
-                       c.col_groups, c.extra, int(aligned(Y, 16) && g.rows % 4 == 0));
+    const int vec = int(aligned(Y, 16) && g.rows % 4 == 0);
+    if (fmt == kMxfp4)
+        hipLaunchKernelGGL(wide_kernel_mxfp4, dim3(unsigned(c.groups)), dim3(kWideWaves * kLanes), kWideLds,
+                           stream, wq, ws, tscale, int(g.rows), int(g.supertiles), int(g.octets), int(g.cols), X, n,
+                           Y, c.row_groups, c.col_groups, c.extra, vec);
+    else
+        hipLaunchKernelGGL(wide_kernel_nvfp4, dim3(unsigned(c.groups)), dim3(kWideWaves * kLanes), kWideLds,
+                           stream, wq, ws, tscale, int(g.rows), int(g.supertiles), int(g.octets), int(g.cols), X, n,
+                           Y, c.row_groups, c.col_groups, c.extra, vec);
     return launch_status();
 }
 

@@ -40,6 +40,8 @@
 // operations of one wave complete in order.
 #pragma once
 
+#include <type_traits>
+
 #include "nvfp4_host.h"
 
 namespace nvfp4 {
@@ -103,18 +105,26 @@ __device__ __forceinline__ unsigned long long argmax_key(float y, uint32_t row) 
 template <int TWW>
 constexpr int scale_loads() { return TWW == 4 ? 1 : TWW; }
 
-// One octet of one wave's operands.
-template <int NC, int TWW>
+// One octet of one wave's operands.  NVFP4 scale entries are 8 bytes per row
+// (the octet's eight 16-element blocks), MXFP4 ones 4 bytes (its four
+// 32-element blocks).
+template <int FMT>
+using ScaleWord = typename std::conditional<FMT == kMxfp4, uint32_t, u32x2>::type;
+
+template <int NC, int TWW, int FMT = kNvfp4>
 struct OctetData {
-    u32x4 code[TWW];                 // lane's 16-byte code entry of each tile
-    u32x2 scale[scale_loads<TWW>()]; // TWW == 4: lane 16tt + r holds tile tt row r; else row r of each tile
-    u32x4 x[NC];                     // compact activations: lane 16c + 4p + q holds X[c][128o + 32p + 8q ..]
+    u32x4 code[TWW];                            // lane's 16-byte code entry of each tile
+    ScaleWord<FMT> scale[scale_loads<TWW>()];   // TWW == 4: lane 16tt + r holds tile tt row r; else row r of each tile
+    u32x4 x[NC];                                // compact activations: lane 16c + 4p + q holds X[c][128o + 32p + 8q ..]
 };
 
 // acc[tt][h]: this wave's share (octets [o0, o1)) of rows 16 (tile) + r of
 // tile tg * TWW + tt of super-tile st, for columns g + 4h (lane = 16g + r).
 // `wl` is the wave's private LDS region of narrow_wave_lds_bytes(N) bytes.
-template <int N, int TWW>
+// FMT kMxfp4: the scale plane holds the four E8M0 bytes of a row's octet; a
+// 32-element slice p is one MX block, so both halves of its MFMA result take
+// that block's scale.
+template <int N, int TWW, int FMT = kNvfp4>
 __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws,
                                                   int64_t st, int tg, int o0, int o1, int octets, int kb,
                                                   const uint16_t *__restrict__ X, int K, int lane,
@@ -123,11 +133,15 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
     constexpr int H = NC;
     const int g = lane >> 4, r = lane & 15;
 
+    static_assert(FMT == kNvfp4 || TWW < 4, "MXFP4 products take one or two tiles per workgroup");
+    constexpr int SREGION = FMT == kMxfp4 ? kMxScaleRegion : kScaleRegion;
+    constexpr int SCHUNK = FMT == kMxfp4 ? kMxScaleChunk : kScaleChunk;
+    constexpr int SROW = FMT == kMxfp4 ? 4 : 8;    // scale bytes per row and octet
     const auto crs = make_rsrc(wq + st * octets * int64_t(kCodeRegion), uint32_t(o1) * kCodeRegion);
-    const auto srs = make_rsrc(ws + st * octets * int64_t(kScaleRegion), uint32_t(o1) * kScaleRegion);
+    const auto srs = make_rsrc(ws + st * octets * int64_t(SREGION), uint32_t(o1) * SREGION);
     const auto xrs = make_rsrc(X, uint32_t(N) * uint32_t(K) * 2u);
     const uint32_t coff = uint32_t(lane * 16 + tg * TWW * kCodeChunk);
-    const uint32_t soff = TWW == 4 ? uint32_t(lane * 8) : uint32_t((tg * TWW * kTileRows + r) * 8);
+    const uint32_t soff = TWW == 4 ? uint32_t(lane * 8) : uint32_t((tg * TWW * kTileRows + r) * SROW);
 
     // Compact activation load of this lane: column xc (+4), k = 128o + 32xp + 8xq.
     const int xc = lane >> 4, xp = (lane >> 2) & 3, xq = lane & 3;
@@ -153,14 +167,18 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
 #pragma unroll
         for (int h = 0; h < H; ++h) part[tt][h][0] = part[tt][h][1] = 0.0f;
 
-    auto load = [&](OctetData<NC, TWW> &d, int o) {
-        const uint32_t co = uint32_t(o) * kCodeRegion + coff, so = uint32_t(o) * kScaleRegion + soff;
+    auto load = [&](OctetData<NC, TWW, FMT> &d, int o) {
+        const uint32_t co = uint32_t(o) * kCodeRegion + coff, so = uint32_t(o) * SREGION + soff;
 #pragma unroll
         for (int tt = 0; tt < TWW; ++tt)
             d.code[tt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, co + tt * kCodeChunk, 0, kStream));
 #pragma unroll
-        for (int tt = 0; tt < scale_loads<TWW>(); ++tt)
-            d.scale[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(srs, so + tt * kScaleChunk, 0, kStream));
+        for (int tt = 0; tt < scale_loads<TWW>(); ++tt) {
+            if constexpr (FMT == kMxfp4)
+                d.scale[tt] = __builtin_amdgcn_raw_buffer_load_b32(srs, so + tt * SCHUNK, 0, kStream);
+            else
+                d.scale[tt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(srs, so + tt * SCHUNK, 0, kStream));
+        }
 #pragma unroll
         for (int h = 0; h < NC; ++h) {
             const uint32_t vo = (o * kOctet + xblk < kb) ? xvo[h] : kOutOfRange;   // ragged last octet
@@ -168,14 +186,17 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
         }
     };
 
-    auto compute = [&](const OctetData<NC, TWW> &d) {
+    auto compute = [&](const OctetData<NC, TWW, FMT> &d) {
 #pragma unroll
         for (int h = 0; h < NC; ++h) xslot[h * kLanes + lane] = d.x[h];
         bf16x8 A[4];   // A operand of block pair p = 2-block slice 32p .. 32p + 31
 #pragma unroll
         for (int p = 0; p < 4; ++p) A[p] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(wl + aoff + 64 * p));
         uint32_t S[2][TWW];   // scale words (blocks 0..3, 4..7 of the octet) of each tile's row r
-        if (TWW == 4) {
+        if constexpr (FMT == kMxfp4) {
+#pragma unroll
+            for (int tt = 0; tt < TWW; ++tt) S[0][tt] = S[1][tt] = d.scale[tt];   // MX blocks 0..3
+        } else if (TWW == 4) {
             uint32_t t0[4], t1[4];
             gather_lane_groups(d.scale[0][0], t0);
             gather_lane_groups(d.scale[0][1], t1);
@@ -202,7 +223,13 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
                                                             floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const float2 sc = e4m3x2_f32(S[p >> 1][tt], p & 1);   // blocks 2p, 2p + 1
+                float2 sc;
+                if constexpr (FMT == kMxfp4) {
+                    const float s = e8m0_f32(S[0][tt] >> (8 * p));   // MX block p holds both halves
+                    sc = float2{s, s};
+                } else {
+                    sc = e4m3x2_f32(S[p >> 1][tt], p & 1);   // blocks 2p, 2p + 1
+                }
                 float &a0 = part[tt][0][p & 1];
                 a0 = __builtin_fmaf(sc.x, D[p][0], a0);
                 a0 = __builtin_fmaf(sc.y, D[p][1], a0);
@@ -217,7 +244,7 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
 
     // Two octets in flight: full iterations prefetch unconditionally (always
     // inside [o0, o1)); the tail covers the last one to three octets.
-    OctetData<NC, TWW> buf[2];
+    OctetData<NC, TWW, FMT> buf[2];
     if (o0 < o1) {
         const int n = o1 - o0;
         load(buf[0], o0);

@@ -182,6 +182,48 @@ int nvfp4_swiglu(const float *gu, int64_t F, int n, uint16_t *h, hipStream_t str
 int nvfp4_gemv_swiglu(const uint8_t *wq_gu, const uint8_t *ws_gu, float tscale, int64_t hidden,
                       int64_t F, const uint16_t *X, int n, float *gu, uint16_t *h, hipStream_t stream);
 
+/* ------------------------------------------------------------------ MXFP4
+ * The second block-scaled format on the same layout and kernels: E2M1 codes
+ * with one power-of-two E8M0 scale byte per 32 elements of a row, the
+ * "E8M0-style" scale the pages set beside NVFP4 (bw24 wiki, feature list;
+ * qwentin README, "Why it's interesting"), read as the OCP Microscaling
+ * MXFP4 format.  Canonical layout: codes [rows][cols/2] (nibble order as
+ * NVFP4), scales [rows][cols/32] (byte b means 2^(b - 127), 0xFF NaN);
+ * cols % 32 == 0 (else NVFP4_ESHAPE).  Repacked layout: the NVFP4 code
+ * plane of the same codes, and a scale plane [ST][O][4 tiles][16 rows][4 B]
+ * whose entry (st, o, tt, r) byte i is the scale of 32-element block 4o + i
+ * of row 64 st + 16 tt + r (zero past the matrix).  The fp32 tensor scale is
+ * a multiplier as for NVFP4.  Error codes and conventions as above. */
+
+/* Sizes of the repacked MXFP4 planes (0 for an invalid shape). */
+size_t mxfp4_repacked_code_bytes(int64_t rows, int64_t cols);
+size_t mxfp4_repacked_scale_bytes(int64_t rows, int64_t cols);
+
+/* Quantise fp32 W [rows][cols] to canonical MXFP4.  Per 32-element block:
+ * E = floor(log2(amax / tscale)) - 2, clamped to [-127, 127] (amax = 0 gives
+ * -127), scale byte E + 127; code = sign bit of w | E2M1 nearest-even of
+ * |w| / (2^E tscale), saturating at 6.  Decisions are exact (fp64). */
+int mxfp4_quantize(const float *W, int64_t rows, int64_t cols, float tscale, uint8_t *codes,
+                   uint8_t *scales, hipStream_t stream);
+
+/* Canonical MXFP4 -> repacked (a byte permutation plus zero padding). */
+int mxfp4_repack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols, uint8_t *wq,
+                 uint8_t *ws, hipStream_t stream);
+
+/* Dequantise repacked MXFP4: out_f32 = e2m1 * 2^(b - 127) * tscale rounded
+ * once to fp32; out_bf16 = e2m1 * 2^(b - 127) (exact, infinite past bf16's
+ * range); NaN scale bytes give NaN.  Either output may be NULL, not both. */
+int mxfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
+                  float *out_f32, uint16_t *out_bf16, hipStream_t stream);
+
+/* nvfp4_gemv for MXFP4 weights: the same products (n <= 8 the matvec with
+ * each 32-element block's dot product on MFMA and its scale in fp32; larger
+ * n the dequant-to-bf16 MFMA contraction, decoding with one scaled
+ * conversion per two elements), the same fixed summation order and column
+ * identity. */
+int mxfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
+               const uint16_t *X, int n, float *Y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -82,6 +82,34 @@ def test_workspace_bytes(lib):
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, (1 << 26) + 16, 4) == 0
 
 
+@pytest.mark.parametrize("rows,cols,code,scale", [
+    (256, 512, 4 * 4 * 4096, 4 * 4 * 256),
+    (17, 32, 1 * 1 * 4096, 1 * 1 * 256),
+    (17408, 5120, 272 * 40 * 4096, 272 * 40 * 256),
+    (65, 160, 2 * 2 * 4096, 2 * 2 * 256),
+])
+def test_mx_plane_sizes(lib, rows, cols, code, scale):
+    assert nv.mxfp4_repacked_code_bytes(rows, cols) == code == nv.nvfp4_repacked_code_bytes(rows, cols)
+    assert nv.mxfp4_repacked_scale_bytes(rows, cols) == scale
+
+
+@pytest.mark.parametrize("rows,cols", [(16, 16), (16, 48), (0, 32), (16, 0)])
+def test_mx_plane_sizes_invalid(lib, rows, cols):
+    assert nv.mxfp4_repacked_code_bytes(rows, cols) == 0
+    assert nv.mxfp4_repacked_scale_bytes(rows, cols) == 0
+
+
+def test_mx_validation(lib):
+    assert lib.mxfp4_gemv(A, B, 1.0, 16, 48, C, 1, A, S0) == ESHAPE       # cols % 32
+    assert lib.mxfp4_gemv(A, B, 1.0, 16, 64, C, 0, A, S0) == EINVAL
+    assert lib.mxfp4_gemv(MIS, B, 1.0, 16, 64, C, 1, A, S0) == EALIGN
+    assert lib.mxfp4_quantize(A, 16, 48, 1.0, B, C, S0) == ESHAPE
+    assert lib.mxfp4_quantize(A, 16, 64, 0.0, B, C, S0) == EINVAL
+    assert lib.mxfp4_repack(A, B, 16, 48, C, A, S0) == ESHAPE
+    assert lib.mxfp4_repack(A, B, 16, 64, C, MIS, S0) == EALIGN
+    assert lib.mxfp4_dequant(A, B, 1.0, 16, 64, NULL, NULL, S0) == EINVAL
+
+
 def test_strerror(lib):
     for code in (OK, EINVAL, ESHAPE, EALIGN, EWORKSPACE, EHIP):
         assert nv.nvfp4_strerror(code)

@@ -1,0 +1,160 @@
+"""GPU parity of the second block-scaled format, MXFP4 (E2M1 codes, one E8M0
+scale per 32 elements), through the C ABI against the oracle's MXFP4 part:
+quantisation and repack bit-exact, dequant exhaustive over every scale byte
+and code, the matvec (n <= 8) and the wide contraction (n > 8) within the
+tolerance, column identity and run-to-run identity."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_scaled_bit_nvfp4_amd as nv
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    nv.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def mx_quantize_gpu(W, tscale=1.0):
+    R, K = W.shape
+    codes = torch.empty(R, K // 2, dtype=torch.uint8, device=G.DEV)
+    scales = torch.empty(R, K // 32, dtype=torch.uint8, device=G.DEV)
+    nv.mxfp4_quantize(W, R, K, tscale, codes, scales)
+    return codes, scales
+
+
+def mx_repack_gpu(codes, scales, R, K):
+    wq, ws = nv.alloc_mx_repacked(R, K, G.DEV)
+    wq.fill_(0xA5)
+    ws.fill_(0x5A)
+    nv.mxfp4_repack(codes, scales, R, K, wq, ws)
+    return wq, ws
+
+
+def mx_gemv_gpu(wq, ws, tscale, R, K, X):
+    n = X.shape[0]
+    Y = torch.full((n, R), float("nan"), dtype=torch.float32, device=G.DEV)
+    nv.mxfp4_gemv(wq, ws, tscale, R, K, X, n, Y)
+    return Y
+
+
+def _prepare(R, K, seed, tscale=1.0, outliers=True):
+    W = G.seeded_matrix(R, K, seed, outliers=outliers)
+    codes, scales = mx_quantize_gpu(W, tscale)
+    c_ref, s_ref = oracle.mx_quantize(W.cpu().numpy(), tscale)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    wq, ws = mx_repack_gpu(codes, scales, R, K)
+    return wq, ws, c_ref, s_ref
+
+
+@pytest.mark.parametrize("R,K,tscale", [(64, 1024, 1.0), (33, 96, 0.37), (100, 2080, 1000.0), (7, 32, 2.0 ** -20)])
+def test_mx_quantize_bitexact(R, K, tscale):
+    W = G.seeded_matrix(R, K, 11 + R)
+    G.note("mx quantize %dx%d" % (R, K))
+    codes, scales = mx_quantize_gpu(W, tscale)
+    c_ref, s_ref = oracle.mx_quantize(W.cpu().numpy(), tscale)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+
+
+def test_mx_quantize_extreme_magnitudes_and_zeros():
+    R, K = 8, 64
+    W = G.seeded_matrix(R, K, 5).cpu()
+    W[0] *= 2.0 ** 100          # large exponents
+    W[1] *= 2.0 ** -120         # the lower clamp
+    W[2] = 0.0
+    W[3] = -0.0
+    W[4, :32] = 3.0e38          # the upper clamp region
+    W = W.to(G.DEV)
+    G.note("mx quantize extremes")
+    codes, scales = mx_quantize_gpu(W)
+    c_ref, s_ref = oracle.mx_quantize(W.cpu().numpy(), 1.0)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+
+
+@pytest.mark.parametrize("R,K", [(17, 32), (16, 1024), (33, 1056), (50, 2080), (256, 512), (65, 160)])
+def test_mx_repack_bytes_equal_reference(R, K):
+    rng = np.random.default_rng(R + K)
+    codes = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 255, (R, K // 32), dtype=np.uint8)
+    G.note("mx repack %dx%d" % (R, K))
+    wq, ws = mx_repack_gpu(torch.from_numpy(codes).to(G.DEV), torch.from_numpy(scales).to(G.DEV), R, K)
+    wq_ref, ws_ref = oracle.mx_repack(codes, scales)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    assert np.array_equal(ws.cpu().numpy(), ws_ref)
+
+
+@pytest.mark.parametrize("tscale", [1.0, 0.37, 2.0 ** -20])
+def test_mx_dequant_every_scale_byte_and_code(tscale):
+    # row b uses scale byte b (b = 255 is NaN); each row holds all 16 codes twice
+    R, K = 256, 32
+    codes = np.tile(np.array([c | ((c + 1) << 4) for c in range(0, 16, 2)] * 2, np.uint8), (R, 1))
+    scales = np.arange(256, dtype=np.uint8)[:, None]
+    wq, ws = mx_repack_gpu(torch.from_numpy(codes).to(G.DEV), torch.from_numpy(scales).to(G.DEV), R, K)
+    f32 = torch.empty(R, K, dtype=torch.float32, device=G.DEV)
+    b16 = torch.empty(R, K, dtype=torch.int16, device=G.DEV)
+    G.note("mx dequant table tscale %g" % tscale)
+    nv.mxfp4_dequant(wq, ws, tscale, R, K, f32, b16)
+    f32, b16 = f32.cpu().numpy(), b16.cpu().numpy().view(np.uint16)
+    with np.errstate(over="ignore"):
+        want32 = oracle.mx_dequant(codes, scales, tscale).astype(np.float32)
+        want16 = (oracle.mx_dequant(codes, scales, 1.0).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    finite = np.arange(R) < 255
+    assert np.array_equal(f32[finite].view(np.uint32), want32[finite].view(np.uint32))
+    assert np.array_equal(b16[finite], want16[finite])
+    assert np.isnan(f32[255]).all()
+    assert np.isnan(b16[255:].view(np.uint16).astype(np.uint32).__lshift__(16).astype(np.uint32).view(np.float32)).all()
+
+
+@pytest.mark.parametrize("R,K,n,tscale", [
+    (256, 512, 1, 1.0), (100, 2080, 1, 1.0), (48, 3072, 2, 0.5), (129, 4096, 3, 1.0), (64, 5120, 4, 1.0),
+    (40, 1024, 5, 2.0), (23, 1088, 6, 1.0), (31, 96, 7, 1.0), (300, 17408, 8, 1.0), (16, 32, 1, 1.0),
+    (4096, 4096, 1, 1.0), (5120, 2048, 4, 1.0),
+])
+def test_mx_gemv_parity(R, K, n, tscale):
+    wq, ws, c_ref, s_ref = _prepare(R, K, 21 + R + K, tscale)
+    X = G.seeded_x(n, K, seed=22 + n)
+    G.note("mx gemv %dx%d n=%d" % (R, K, n))
+    Y = mx_gemv_gpu(wq, ws, tscale, R, K, X).cpu().numpy()
+    Y_ref, S = oracle.mx_gemv(c_ref, s_ref, tscale, G.wl.bf16_bits(X))
+    G.assert_within_tolerance(Y, Y_ref, S, "mx gemv %dx%d n=%d" % (R, K, n))
+
+
+@pytest.mark.parametrize("R,K,n", [(80, 1024, 12), (1000, 1056, 130), (257, 2080, 9), (17, 32, 300),
+                                   (4096, 512, 256), (17408, 640, 512)])
+def test_mx_gemv_wide_parity(R, K, n):
+    wq, ws, c_ref, s_ref = _prepare(R, K, 77 + R + K)
+    X = G.seeded_x(n, K, seed=78 + n)
+    G.note("mx gemv wide %dx%d n=%d" % (R, K, n))
+    Y = mx_gemv_gpu(wq, ws, 1.0, R, K, X).cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(min(R, 48)), np.arange(max(0, R - 48), R),
+                                     np.random.default_rng(R).choice(R, size=min(R, 256), replace=False)]))
+    Y_ref, S = oracle.mx_gemv_rows(c_ref, s_ref, 1.0, G.wl.bf16_bits(X), rows)
+    G.assert_within_tolerance(Y[:, rows], Y_ref, S, "mx gemv wide %dx%d n=%d" % (R, K, n))
+
+
+def test_mx_gemv_deterministic_and_column_identity():
+    R, K = 1040, 5120
+    wq, ws, _, _ = _prepare(R, K, 9)
+    X = G.seeded_x(8, K, seed=10)
+    G.note("mx gemv determinism")
+    ys = {}
+    for n in (1, 2, 4, 8):
+        ys[n] = mx_gemv_gpu(wq, ws, 1.0, R, K, X[:n].contiguous())
+        again = mx_gemv_gpu(wq, ws, 1.0, R, K, X[:n].contiguous())
+        assert torch.equal(ys[n].view(torch.int32), again.view(torch.int32)), n
+    for c in range(8):
+        single = mx_gemv_gpu(wq, ws, 1.0, R, K, X[c:c + 1].contiguous())
+        for n in (2, 4, 8):
+            if c < n:
+                assert torch.equal(ys[n][c].view(torch.int32), single[0].view(torch.int32)), (c, n)
