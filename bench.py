@@ -42,27 +42,44 @@ def log(msg):
 # ------------------------------------------------------------------ set-up --
 
 class Matrix:
-    """A repacked NVFP4 matrix resident in HBM (quantised and repacked by the
-    library from seeded fp32 weights; set-up, not timed)."""
+    """A repacked NVFP4 (or MXFP4) matrix resident in HBM (quantised and
+    repacked by the library from seeded fp32 weights; set-up, not timed)."""
 
     def __init__(self, workload, m, copy):
         W = wl.weights(m.rows, m.cols, seed=wl.seed_of(workload.name, m.name, copy),
                        outliers=workload.outliers, device=DEV)
+        self.fmt = workload.fmt
         codes = torch.empty(m.rows, m.cols // 2, dtype=torch.uint8, device=DEV)
-        scales = torch.empty(m.rows, m.cols // 16, dtype=torch.uint8, device=DEV)
-        nv.nvfp4_quantize(W, m.rows, m.cols, workload.tscale, codes, scales)
-        self.wq, self.ws = nv.alloc_repacked(m.rows, m.cols, DEV)
-        nv.nvfp4_repack(codes, scales, m.rows, m.cols, self.wq, self.ws)
+        if self.fmt == "mxfp4":
+            scales = torch.empty(m.rows, m.cols // 32, dtype=torch.uint8, device=DEV)
+            nv.mxfp4_quantize(W, m.rows, m.cols, workload.tscale, codes, scales)
+            self.wq, self.ws = nv.alloc_mx_repacked(m.rows, m.cols, DEV)
+            nv.mxfp4_repack(codes, scales, m.rows, m.cols, self.wq, self.ws)
+        else:
+            scales = torch.empty(m.rows, m.cols // 16, dtype=torch.uint8, device=DEV)
+            nv.nvfp4_quantize(W, m.rows, m.cols, workload.tscale, codes, scales)
+            self.wq, self.ws = nv.alloc_repacked(m.rows, m.cols, DEV)
+            nv.nvfp4_repack(codes, scales, m.rows, m.cols, self.wq, self.ws)
         self.rows, self.cols, self.name, self.copy = m.rows, m.cols, m.name, copy
         self.tscale = workload.tscale
 
     def weight_bytes(self):
-        return self.rows * self.cols * 9 // 16          # 0.5625 B per element
+        return weight_bytes(self.rows, self.cols, self.fmt)
+
+    def gemv(self, x, n, y):
+        f = nv.mxfp4_gemv if self.fmt == "mxfp4" else nv.nvfp4_gemv
+        f(self.wq, self.ws, self.tscale, self.rows, self.cols, x, n, y)
 
 
-def gemv_bytes(rows, cols, n):
+def weight_bytes(rows, cols, fmt="nvfp4"):
+    """Code and scale bytes: 0.5625 B per element for NVFP4 (a scale per 16),
+    0.53125 for MXFP4 (a scale per 32)."""
+    return rows * cols * 17 // 32 if fmt == "mxfp4" else rows * cols * 9 // 16
+
+
+def gemv_bytes(rows, cols, n, fmt="nvfp4"):
     """Algorithmic bytes of one product: weights + X + Y."""
-    return rows * cols * 9 // 16 + n * cols * 2 + n * rows * 4
+    return weight_bytes(rows, cols, fmt) + n * cols * 2 + n * rows * 4
 
 
 class Step:
@@ -126,12 +143,20 @@ class Step:
             for i, M in enumerate(self.mats):
                 self.launches.append((self._argmax_of(M, self.logits2[i % 2], self.am2[i % 2]),
                                       gemv_bytes(M.rows, M.cols, 1) + 4, 2 * M.rows * M.cols, "gemv"))
-        elif name == "prefill_n512":
+        elif name == "mxfp4_gemv_17408x5120":
+            m = w.matrices[0]
+            self.x = wl.activations(1, m.cols, seed=wl.seed_of(name, "x"), device=DEV)
+            self.mats = [Matrix(w, m, c) for c in range(w.copies)]
+            self.ys = [torch.empty(1, m.rows, dtype=torch.float32, device=DEV) for _ in range(2)]
+            for i, M in enumerate(self.mats):
+                self.launches.append((self._gemv(M, self.x, 1, self.ys[i % 2]), gemv_bytes(M.rows, M.cols, 1, "mxfp4"),
+                                      2 * M.rows * M.cols, "gemv"))
+        elif name in ("prefill_n512", "mxfp4_prefill_n512"):
             m = w.matrices[0]
             self.x = wl.activations(512, m.cols, seed=wl.seed_of(name, "x"), device=DEV)
             self.M = Matrix(w, m, 0)
             self.y = torch.empty(512, m.rows, dtype=torch.float32, device=DEV)
-            self.launches.append((self._gemv(self.M, self.x, 512, self.y), gemv_bytes(m.rows, m.cols, 512),
+            self.launches.append((self._gemv(self.M, self.x, 512, self.y), gemv_bytes(m.rows, m.cols, 512, w.fmt),
                                   2 * 512 * m.rows * m.cols, "gemm"))
         else:
             raise SystemExit("unknown workload %r (choose from %s)" % (name, ", ".join(wl.WORKLOADS)))
@@ -143,7 +168,7 @@ class Step:
     @staticmethod
     def _gemv(M, x, n, y):
         def f():
-            nv.nvfp4_gemv(M.wq, M.ws, M.tscale, M.rows, M.cols, x, n, y)
+            M.gemv(x, n, y)
         return f
 
     def _gemv_swiglu(self, G_, Dh, F):
@@ -223,8 +248,11 @@ def cpu_baseline(step, budget_s=12.0):
     elif w.name == "verify_vocab_n4":
         sample.append((step.M1, step.x, None))
         sample.append((step.M2, step.x, np.arange(0, step.M2.rows, 8)))
-    elif w.name == "prefill_n512":
+    elif w.name in ("prefill_n512", "mxfp4_prefill_n512"):
         sample.append((step.M, step.x, np.arange(0, step.M.rows, 256)))
+    elif w.name == "mxfp4_gemv_17408x5120":
+        for M in step.mats:
+            sample.append((M, step.x, None))
     elif w.name == "draft_head_8192x4096":
         for M in step.mats:
             sample.append((M, step.x, None))
@@ -237,19 +265,20 @@ def cpu_baseline(step, budget_s=12.0):
         rsel = np.arange(M.rows) if rows is None else rows
         Wh = Wf[torch.as_tensor(rsel, device=DEV)].cpu().numpy()
         del Wf
-        codes, scales = oracle.quantize(Wh, w.tscale)
+        quantize = oracle.mx_quantize if w.fmt == "mxfp4" else oracle.quantize
+        codes, scales = quantize(Wh, w.tscale)
         key = id(x)
         if key not in xb_cache:
             xb_cache[key] = wl.bf16_bits(x)
         xb = xb_cache[key]
         n = x.shape[0]
         t0 = time.perf_counter()
-        Y_ref, S = oracle.gemv(codes, scales, w.tscale, xb)
+        Y_ref, S = (oracle.mx_gemv if w.fmt == "mxfp4" else oracle.gemv)(codes, scales, w.tscale, xb)
         dt = time.perf_counter() - t0
         t_total += dt
-        bytes_done += gemv_bytes(len(rsel), M.cols, n)
+        bytes_done += gemv_bytes(len(rsel), M.cols, n, w.fmt)
         y = torch.empty(n, M.rows, dtype=torch.float32, device=DEV)
-        nv.nvfp4_gemv(M.wq, M.ws, M.tscale, M.rows, M.cols, x, n, y)
+        M.gemv(x, n, y)
         yg = y.cpu().numpy()[:, rsel].astype(np.float64)
         err = np.abs(yg - Y_ref) / (1e-5 * S + 1e-6)
         worst = max(worst, float(err.max()))
@@ -334,7 +363,7 @@ def main():
     # divided by the launches is the average launch duration; otherwise the
     # figure covers the whole step and says so.
     tags = {t for _, _, _, t in step.launches}
-    kernel = "gemm" if args.workload == "prefill_n512" else "gemv"
+    kernel = "gemm" if args.workload in ("prefill_n512", "mxfp4_prefill_n512") else "gemv"
     n_launch = sum(1 for _, _, _, t in step.launches if t == kernel)
     per_launch_s = step_ev_s / n_launch
     if args.workload == "draft_head_8192x4096":

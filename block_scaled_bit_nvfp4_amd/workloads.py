@@ -46,6 +46,7 @@ class Workload:
     outliers: bool = True
     tscale: float = 1.0
     argmax: tuple = field(default_factory=tuple)   # names of matrices with an argmax
+    fmt: str = "nvfp4"         # weight format: "nvfp4" or "mxfp4"
 
 
 WORKLOADS = {
@@ -74,6 +75,15 @@ WORKLOADS = {
         "draft_head_8192x4096", "trimmed-vocabulary draft head 8192x4096 with argmax, N=1; "
         "16 distinct heads rotated",
         1, (Matrix("draft_head", 8192, 4096),), copies=16, argmax=("draft_head",)),
+    # The second block-scaled format (E2M1 with one E8M0 scale per 32
+    # elements) on the 17408 x 5120 matrix: N = 1 over 8 rotated copies
+    # (379 MB, past the Infinity Cache), and the N = 512 contraction.
+    "mxfp4_gemv_17408x5120": Workload(
+        "mxfp4_gemv_17408x5120", "MXFP4 matvec 17408x5120, N=1, 8 distinct matrices rotated",
+        1, (Matrix("w", 17408, 5120),), copies=8, fmt="mxfp4"),
+    "mxfp4_prefill_n512": Workload(
+        "mxfp4_prefill_n512", "MXFP4 prefill-width contraction N=512: 17408x5120",
+        512, (Matrix("w", 17408, 5120),), copies=1, fmt="mxfp4"),
 }
 
 

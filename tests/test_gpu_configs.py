@@ -177,3 +177,51 @@ def test_draft_head_8192x4096_full_argmax():
         # the argmax without stored logits names the same row
         _, am2 = G.gemv_argmax_gpu(q, ss, w.tscale, m.rows, m.cols, X, with_logits=False)
         assert torch.equal(am, am2)
+
+
+def _mx_matrix(workload, m, copy=0):
+    import block_scaled_bit_nvfp4_amd as nv
+    W = wl.weights(m.rows, m.cols, seed=wl.seed_of(workload.name, m.name, copy),
+                   outliers=workload.outliers, device=G.DEV)
+    codes = torch.empty(m.rows, m.cols // 2, dtype=torch.uint8, device=G.DEV)
+    scales = torch.empty(m.rows, m.cols // 32, dtype=torch.uint8, device=G.DEV)
+    nv.mxfp4_quantize(W, m.rows, m.cols, workload.tscale, codes, scales)
+    wq, ws = nv.alloc_mx_repacked(m.rows, m.cols, G.DEV)
+    nv.mxfp4_repack(codes, scales, m.rows, m.cols, wq, ws)
+    return W, codes, scales, wq, ws
+
+
+def test_mxfp4_gemv_17408x5120_full():
+    import block_scaled_bit_nvfp4_amd as nv
+    w = wl.WORKLOADS["mxfp4_gemv_17408x5120"]
+    m = w.matrices[0]
+    X = wl.activations(1, m.cols, seed=wl.seed_of(w.name, "x"), device=G.DEV)
+    for copy in (0, w.copies - 1):
+        G.note("config mxfp4_gemv_17408x5120 copy %d" % copy)
+        W, c, s, q, ss = _mx_matrix(w, m, copy)
+        Y = torch.full((1, m.rows), float("nan"), dtype=torch.float32, device=G.DEV)
+        nv.mxfp4_gemv(q, ss, w.tscale, m.rows, m.cols, X, 1, Y)
+        c_ref, s_ref = oracle.mx_quantize(W.cpu().numpy(), w.tscale)
+        assert np.array_equal(c.cpu().numpy(), c_ref)
+        assert np.array_equal(s.cpu().numpy(), s_ref)
+        Y_ref, S = oracle.mx_gemv(c_ref, s_ref, w.tscale, wl.bf16_bits(X))
+        G.assert_within_tolerance(Y.cpu().numpy(), Y_ref, S, "mxfp4 17408x5120")
+
+
+def test_mxfp4_prefill_n512_sampled():
+    import block_scaled_bit_nvfp4_amd as nv
+    w = wl.WORKLOADS["mxfp4_prefill_n512"]
+    m = w.matrices[0]
+    X = wl.activations(512, m.cols, seed=wl.seed_of(w.name, "x"), device=G.DEV)
+    G.note("config mxfp4_prefill_n512")
+    W, c, s, q, ss = _mx_matrix(w, m)
+    Y = torch.full((512, m.rows), float("nan"), dtype=torch.float32, device=G.DEV)
+    nv.mxfp4_gemv(q, ss, w.tscale, m.rows, m.cols, X, 512, Y)
+    rows = _sample_rows(m.rows, 256, 5)
+    Wr = W[torch.as_tensor(rows, device=W.device)].cpu().numpy()
+    c_ref, s_ref = oracle.mx_quantize(Wr, w.tscale)
+    idx = torch.as_tensor(rows, device=G.DEV)
+    assert np.array_equal(c[idx].cpu().numpy(), c_ref)
+    assert np.array_equal(s[idx].cpu().numpy(), s_ref)
+    Y_ref, S = oracle.mx_gemv_rows(c_ref, s_ref, w.tscale, wl.bf16_bits(X))
+    G.assert_within_tolerance(Y.cpu().numpy()[:, rows], Y_ref, S, "mxfp4 prefill n512")

@@ -7,7 +7,10 @@ from block_scaled_bit_nvfp4_amd import workloads as wl
 
 def test_workload_table():
     assert set(wl.WORKLOADS) == {"gemv_256x512", "decode_4096x4096", "mlp_27b_decode",
-                                 "verify_vocab_n4", "prefill_n512", "draft_head_8192x4096"}
+                                 "verify_vocab_n4", "prefill_n512", "draft_head_8192x4096",
+                                 "mxfp4_gemv_17408x5120", "mxfp4_prefill_n512"}
+    assert wl.WORKLOADS["mxfp4_prefill_n512"].fmt == "mxfp4"
+    assert wl.WORKLOADS["prefill_n512"].fmt == "nvfp4"
     d = wl.WORKLOADS["draft_head_8192x4096"]
     assert (d.matrices[0].rows, d.matrices[0].cols, d.n, d.copies) == (8192, 4096, 1, 16)
     assert d.argmax == ("draft_head",)
