@@ -154,10 +154,12 @@ class Step:
         elif name in ("prefill_n512", "mxfp4_prefill_n512"):
             m = w.matrices[0]
             self.x = wl.activations(512, m.cols, seed=wl.seed_of(name, "x"), device=DEV)
-            self.M = Matrix(w, m, 0)
-            self.y = torch.empty(512, m.rows, dtype=torch.float32, device=DEV)
-            self.launches.append((self._gemv(self.M, self.x, 512, self.y), gemv_bytes(m.rows, m.cols, 512, w.fmt),
-                                  2 * 512 * m.rows * m.cols, "gemm"))
+            self.mats = [Matrix(w, m, c) for c in range(w.copies)]
+            self.M = self.mats[0]
+            self.ys = [torch.empty(512, m.rows, dtype=torch.float32, device=DEV) for _ in range(2)]
+            for i, M in enumerate(self.mats):
+                self.launches.append((self._gemv(M, self.x, 512, self.ys[i % 2]),
+                                      gemv_bytes(m.rows, m.cols, 512, w.fmt), 2 * 512 * m.rows * m.cols, "gemm"))
         else:
             raise SystemExit("unknown workload %r (choose from %s)" % (name, ", ".join(wl.WORKLOADS)))
         torch.cuda.synchronize()

@@ -9,7 +9,9 @@
 // scales, which cannot hold an E4M3 x fp32 scale exactly, so the weights are
 // decoded to bf16 values e2m1 * e4m3 (exact: at most 6 significant bits) and
 // multiplied on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the tensor
-// scale multiplies the result.
+// scale multiplies the result.  The same body, instantiated for MXFP4, reads
+// one E8M0 byte per 32 elements and decodes e2m1 * 2^(b - 127) in the scaled
+// conversion itself (exact for every finite byte).
 //
 // Tiling.  Two waves per SIMD, so that one wave's weight decode (VALU) runs
 // while the other's MFMAs execute.  A workgroup of eight waves owns four

@@ -65,9 +65,11 @@ WORKLOADS = {
         "with per-column argmax",
         4, (Matrix("w", 17408, 5120), Matrix("lm_head", 151936, 5120)), copies=1,
         argmax=("lm_head",)),
+    # The N = 512 contraction runs over four layer copies per step, so that a
+    # step's launches run back to back as a prefill's layers would.
     "prefill_n512": Workload(
-        "prefill_n512", "prefill-width contraction N=512: 17408x5120",
-        512, (Matrix("w", 17408, 5120),), copies=1),
+        "prefill_n512", "prefill-width contraction N=512: 17408x5120, 4 layer copies rotated",
+        512, (Matrix("w", 17408, 5120),), copies=4),
     # A trimmed-vocabulary draft head (an 8192-row subset of a vocabulary at a
     # 4096 hidden size: 18.9 MB at NVFP4) drafting one token per call;
     # 16 copies (302 MB) rotate past the 256 MB Infinity Cache.
@@ -82,8 +84,8 @@ WORKLOADS = {
         "mxfp4_gemv_17408x5120", "MXFP4 matvec 17408x5120, N=1, 8 distinct matrices rotated",
         1, (Matrix("w", 17408, 5120),), copies=8, fmt="mxfp4"),
     "mxfp4_prefill_n512": Workload(
-        "mxfp4_prefill_n512", "MXFP4 prefill-width contraction N=512: 17408x5120",
-        512, (Matrix("w", 17408, 5120),), copies=1, fmt="mxfp4"),
+        "mxfp4_prefill_n512", "MXFP4 prefill-width contraction N=512: 17408x5120, 4 layer copies rotated",
+        512, (Matrix("w", 17408, 5120),), copies=4, fmt="mxfp4"),
 }
 
 
