@@ -63,14 +63,12 @@ constexpr int kXDmaPerWave = kXBuf / (kWideWaves * kLanes * 16);   // 16-byte la
 // One octet of the workgroup's weights in LDS: per wave its two code chunks
 // and its tiles' scale bytes as two dword planes; then, for each of the
 // waves that decode the extra tile (one 32-k slice each), its own copy of
-// the extra tile's code chunk and scale bytes; and a scratch run for the
-// placeholder loads that keep every wave's load count equal.
+// the extra tile's code chunk and scale bytes.
 constexpr int kWWave = kWaveTiles * kCodeChunk + 2 * 256;   // 2.5 KiB
 constexpr int kXDecoders = 4;                   // waves decoding the extra tile, one slice each
 constexpr int kWXWave = kCodeChunk + 256;       // a decoder's raw extra tile: code, then 128 scale bytes
 constexpr int kWXCode = kWideWaves * kWWave;
-constexpr int kWDummy = kWXCode + kXDecoders * kWXWave;
-constexpr int kWStage = kWDummy + 256;
+constexpr int kWStage = kWXCode + kXDecoders * kWXWave;
 constexpr int kWRing = 3;                       // octets of weights in LDS
 // The extra tile's decoded A operands of one octet: 4 slices x 64 lanes x
 // 16 bytes, in a ring of two octets.
@@ -186,45 +184,56 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
         }
     };
     // Weights of octet o into ring stage o % 3: this wave's two code chunks
-    // (lane l's 16 bytes of tile j at 1024 j + 16 l), its tiles' 256 scale
-    // bytes as low and high dwords of lanes 0 .. 31 (lane 16 j + r: row r of
-    // tile j), and for a decoder wave its own copy of the extra tile's code
-    // chunk and scale bytes (two placeholder loads for the other waves).
+    // (lane l's 16 bytes of tile j at 1024 j + 16 l), its tiles' scale bytes
+    // (NVFP4: 256 as low and high dwords of lanes 0 .. 31, lane 16 j + r
+    // holding row r of tile j; MXFP4: 128 as one dword of those lanes), and
+    // for a decoder wave its own copy of the extra tile's code chunk and
+    // scale bytes.  Every load has its own source and destination, so the
+    // compiler cannot merge two of them: the waits below count them.
     uint8_t *const wring = xs + kXRing * kXBuf;
     uint8_t *const xaring = wring + kWRing * kWStage;
-    auto load_w = [&](int o) {
+    // Part 0: the code chunks; part 1: the own scale bytes; part 2: the
+    // extra tile's bytes (decoder waves only).
+    auto load_w_part = [&](int o, int part) {
         uint8_t *dst = wring + (o % kWRing) * kWStage;
         uint8_t *mine = dst + wave * kWWave;
         const uint32_t co = uint32_t(o) * kCodeRegion + uint32_t(lane) * 16u;
+        if (part == 0) {
 #pragma unroll
-        for (int j = 0; j < kWaveTiles; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, lds_ptr(mine + j * kCodeChunk), 16, co + j * kCodeChunk, 0, 0,
-                                                     kStream);
+            for (int j = 0; j < kWaveTiles; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, lds_ptr(mine + j * kCodeChunk), 16, co + j * kCodeChunk,
+                                                         0, 0, kStream);
+        } else if (part == 1) {
         if constexpr (FMT == kMxfp4) {
-            // one dword per row (lane 16 j + r: row r of tile j), and a
-            // placeholder load for an equal count
             const uint32_t so = lane < 32 ? uint32_t(o) * SREGION + uint32_t(lane) * 4u : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk), 4, so, 0, 0, kStream);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(dst + kWDummy), 4, kOutOfRange, 0, 0, kStream);
         } else {
             const uint32_t so = lane < 32 ? uint32_t(o) * SREGION + uint32_t(lane) * 8u : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk), 4, so, 0, 0, kStream);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk + 256), 4,
                                                      so == kOutOfRange ? so : so + 4, 0, 0, kStream);
         }
-        if (wave < kXDecoders) {
+        } else if (wave < kXDecoders) {
             uint8_t *xw = dst + kWXCode + wave * kWXWave;
             // the extra tile's 16 rows of scale bytes: 8 per row (NVFP4) or 4 (MXFP4)
             const int xlanes = FMT == kMxfp4 ? 16 : 32;
             const uint32_t xso = lane < xlanes ? uint32_t(o) * SREGION + uint32_t(lane) * 4u : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xcrs, lds_ptr(xw), 16, co, 0, 0, kStream);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(xw + kCodeChunk), 4, xso, 0, 0, kStream);
-        } else {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(dst + kWDummy), 4, kOutOfRange, 0, 0, kStream);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xsrs, lds_ptr(dst + kWDummy), 4, kOutOfRange, 0, 0, kStream);
         }
     };
-    constexpr int kWLoads = kWaveTiles + 4;   // vector-memory operations of load_w per wave
+    auto load_w = [&](int o) {
+        load_w_part(o, 0);
+        load_w_part(o, 1);
+        load_w_part(o, 2);
+    };
+    // Vector-memory operations of load_w: a decoder wave issues the extra
+    // tile's two loads on top of its own.  (A wave's loads complete in
+    // issue order; the waits below leave exactly the newest load_w
+    // outstanding, so everything issued before it has landed in LDS.)
+    constexpr int kWLoadsOwn = kWaveTiles + (FMT == kMxfp4 ? 1 : 2);
+    constexpr int kWLoadsDec = kWLoadsOwn + 2;
+    const bool xdecoder = wave < kXDecoders;   // issues the extra tile's loads (zeros when there is none)
     // A decoder wave turns slice d = wave of the extra tile's octet o into
     // exact bf16 A operands for every lane, from its own copy of the raw
     // bytes, into the extra ring (published by the next barrier).
@@ -256,7 +265,10 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
     for (int d = 0; d < 4; ++d) boff[d] = xtile_offset(c16, 4 * d + g);
     const uint32_t xboff = uint32_t(wave * 16 * kXColBytes);
 
-    auto compute = [&](int o, auto extra_c) {
+    // wo >= 0: the weight loads of octet wo are issued in three parts at the
+    // starts of slices 1, 2 and 3, after this octet's X loads and spread
+    // between the MFMAs instead of in one burst after the barrier.
+    auto compute = [&](int o, auto extra_c, int wo) {
         constexpr bool EXTRA = decltype(extra_c)::value;   // wave-uniform, fixed per workgroup
         const uint8_t *wst = wring + (o % kWRing) * kWStage;
         const uint8_t *mine = wst + wave * kWWave;
@@ -308,6 +320,7 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
             // ahead and idles at the barrier while the other finishes alone.
             if (((d + (wave >> 2)) & 1) != 0) __builtin_amdgcn_s_setprio(2);
             else __builtin_amdgcn_s_setprio(0);
+            if (d >= 1 && wo >= 0) load_w_part(wo, d - 1);
 #pragma unroll
             for (int cs = 0; cs < kWideSub; ++cs) {
 #pragma unroll
@@ -327,39 +340,50 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
     };
 
     // Octet o is multiplied from X buffer o % 2 and weight stage o % 3.  At
-    // octet o a wave issues octet o + 1's X loads, then octet o + 2's weight
-    // loads, so at the start of octet o + 1 only the latter may still be
-    // outstanding: the wait below finishes this wave's loads of the octet
-    // about to be used (and its LDS writes), and the barrier publishes every
-    // wave's loads and decoded extra operands and frees the buffers restaged
-    // next (read at octet o - 1).  A bare barrier: __syncthreads() would also
-    // drain every outstanding load (its fence), emptying the rings; the
-    // memory clobber keeps the LDS accesses on their side of it.  A decoder
-    // wave decodes octet o + 1's extra slice after octet o's MFMAs, once its
-    // own octet o + 1 weight loads (issued an octet earlier) are done.
+    // octet o a wave issues octet o + 1's X loads, then (spread over the
+    // slices) octet o + 2's weight loads, so at the start of octet o + 1 only
+    // the latter may still be outstanding: the wait below leaves exactly
+    // those outstanding (the wave's own load_w count), which finishes the
+    // loads of the octet about to be used and their LDS writes, and the
+    // barrier publishes every wave's loads and decoded extra operands and
+    // frees the buffers restaged next (read at octet o - 1).  A bare barrier:
+    // __syncthreads() would also drain every outstanding load (its fence),
+    // emptying the rings; the memory clobber keeps the LDS accesses on their
+    // side of it.  A decoder wave decodes octet o + 1's extra slice after
+    // octet o's MFMAs, once its own octet o + 1 weight loads (issued an octet
+    // earlier) are done.  The compiler barriers between the load groups keep
+    // the X and weight loads in program order, which the counts rely on.
+    auto fence = [] { asm volatile("" ::: "memory"); };
     auto run = [&](auto extra_c) {
         constexpr bool EXTRA = decltype(extra_c)::value;
-        const bool decoder = EXTRA && wave < kXDecoders;
+        const bool decoder = EXTRA && xdecoder;
         load_w(0);
+        fence();
         stage_x(0);
+        fence();
         if (octets > 1) load_w(1);
+        fence();
         if (decoder) {
-            if (octets > 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoads));
+            if (octets > 1) __builtin_amdgcn_s_waitcnt(vmcnt_only(kWLoadsDec));
             else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-            asm volatile("" ::: "memory");   // the raw bytes' LDS reads stay below the wait
+            fence();   // the raw bytes' LDS reads stay below the wait
             decode_extra(0);
         }
         for (int o = 0; o < octets; ++o) {
-            if (o + 1 < octets) __builtin_amdgcn_s_waitcnt(vmcnt_lds(kWLoads));
-            else __builtin_amdgcn_s_waitcnt(0);
+            if (o + 1 < octets) {
+                if (xdecoder) __builtin_amdgcn_s_waitcnt(vmcnt_lds(kWLoadsDec));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_lds(kWLoadsOwn));
+            } else {
+                __builtin_amdgcn_s_waitcnt(0);
+            }
             asm volatile("s_barrier" ::: "memory");
             if (o + 1 < octets) stage_x(o + 1);
-            if (o + 2 < octets) load_w(o + 2);
-            compute(o, extra_c);
+            fence();
+            compute(o, extra_c, o + 2 < octets ? o + 2 : -1);
             if (decoder && o + 1 < octets) {
-                if (o + 2 < octets) __builtin_amdgcn_s_waitcnt(vmcnt_only(kXDmaPerWave + kWLoads));
+                if (o + 2 < octets) __builtin_amdgcn_s_waitcnt(vmcnt_only(kXDmaPerWave + kWLoadsDec));
                 else __builtin_amdgcn_s_waitcnt(vmcnt_only(kXDmaPerWave));
-                asm volatile("" ::: "memory");
+                fence();
                 decode_extra(o + 1);
             }
         }

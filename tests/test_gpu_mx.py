@@ -158,3 +158,29 @@ def test_mx_gemv_deterministic_and_column_identity():
         for n in (2, 4, 8):
             if c < n:
                 assert torch.equal(ys[n][c].view(torch.int32), single[0].view(torch.int32)), (c, n)
+
+
+@pytest.mark.parametrize("R,K,n", [(4160, 2048, 300), (17408, 5120, 512)])
+def test_mx_wide_repeat_bit_identical(R, K, n):
+    """Forty back-to-back launches of the MXFP4 wide product give the same
+    bits as the first, which matches the oracle on sampled rows (see the
+    NVFP4 twin of this test for what a missed wait looks like)."""
+    W = G.seeded_matrix(R, K, 25)
+    codes, scales = mx_quantize_gpu(W)
+    wq, ws = mx_repack_gpu(codes, scales, R, K)
+    X = G.seeded_x(n, K, seed=26)
+    G.note("mx wide repeat %dx%d n=%d" % (R, K, n))
+    first = mx_gemv_gpu(wq, ws, 1.0, R, K, X)
+    Y = torch.empty_like(first)
+    for i in range(40):
+        Y.fill_(float("nan"))
+        nv.mxfp4_gemv(wq, ws, 1.0, R, K, X, n, Y)
+        assert torch.equal(Y.view(torch.int32), first.view(torch.int32)), "launch %d differs" % i
+    rows = np.unique(np.concatenate([np.arange(32), np.arange(R - 32, R),
+                                     np.random.default_rng(R).choice(R, size=96, replace=False)]))
+    idx = torch.as_tensor(rows, device=W.device)
+    c_ref, s_ref = oracle.mx_quantize(W[idx].cpu().numpy(), 1.0)
+    assert np.array_equal(codes[idx].cpu().numpy(), c_ref)
+    assert np.array_equal(scales[idx].cpu().numpy(), s_ref)
+    Y_ref, S = oracle.mx_gemv_rows(c_ref, s_ref, 1.0, G.wl.bf16_bits(X))
+    G.assert_within_tolerance(first.cpu().numpy()[:, rows], Y_ref, S, "mx wide repeat %dx%d n=%d" % (R, K, n))
