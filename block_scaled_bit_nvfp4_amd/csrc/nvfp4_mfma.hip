@@ -22,9 +22,9 @@
 // direct-to-LDS buffer loads, XOR-swizzled by 16-byte chunk so that the
 // B-operand reads of 16 neighbouring columns hit distinct banks; the weights
 // go the same way into a ring of three stages, two octets ahead of the
-// MFMAs.  The two waves of a SIMD take turns at the higher issue priority
-// slice by slice, which keeps them level at the per-octet barrier.  Word d of a lane's 16-byte code entry of a tile is directly the A
-// operand of k = 128o + 32d .. +31 (lane 16g + r: row r, elements
+// MFMAs, their loads spread over the slices of an octet.  Word d of a
+// lane's 16-byte code entry of a tile is directly the A operand of
+// k = 128o + 32d .. +31 (lane 16g + r: row r, elements
 // 8g .. 8g + 7), decoded to exact bf16 in registers with its E4M3 scale.  A
 // decoded A operand feeds eight MFMAs (the column subtiles); the next slice's
 // A operands are decoded, and each B operand is re-read for the next slice,
@@ -315,11 +315,6 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int cur = d & 1, nxt = cur ^ 1;
-            // Waves w and w + 4 share a SIMD; they take turns at the higher
-            // issue priority slice by slice, so neither runs a whole octet
-            // ahead and idles at the barrier while the other finishes alone.
-            if (((d + (wave >> 2)) & 1) != 0) __builtin_amdgcn_s_setprio(2);
-            else __builtin_amdgcn_s_setprio(0);
             if (d >= 1 && wo >= 0) load_w_part(wo, d - 1);
 #pragma unroll
             for (int cs = 0; cs < kWideSub; ++cs) {
@@ -390,7 +385,6 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
     };
     if (has_extra) run(std::true_type{});
     else run(std::false_type{});
-    __builtin_amdgcn_s_setprio(0);
 
     // Lane (g, c16) holds rows 4g .. 4g + 3 of a tile for column
     // cs * 16 + c16 of the column tile.
