@@ -54,16 +54,20 @@ constexpr int64_t kMaxNarrowCols = int64_t(1) << 26;
 
 // Decomposition of a rows x cols product over workgroups; a function of the
 // shape only.  Measured on the workload shapes (decode 4096 x 4096, the MLP's
-// 34816 x 5120 and 5120 x 17408, the 17408 x 5120 verify matrix and the
-// 151936 x 5120 vocabulary head): the narrow kernel keeps enough bytes in
-// flight with eight waves of two tiles per workgroup, except that
+// 34816 x 5120 and 5120 x 17408, the 17408 x 5120 verify matrix, the
+// 151936 x 5120 vocabulary head and the 8192 x 4096 draft head) and on
+// 320..1024-tile sweeps at 4096 and 5120 columns: the narrow kernel keeps
+// enough bytes in flight with eight waves of two tiles per workgroup, except
+// that
 //   - small matrices (<= 256 tiles) want one tile per workgroup and sixteen
 //     waves, so that every CU gets a workgroup and each wave a short chain;
+//     up to 512 tiles this still pays while each of the sixteen waves has at
+//     most two octets (both loaded before the first is used);
 //   - mid-size ones (512 < tiles <= 4096) run best with one tile and eight
 //     waves, which also keeps the fused gate||up+SwiGLU workgroup (two sets of
 //     waves) at two workgroups per CU.
-// Shapes between 256 and 512 tiles take two tiles per workgroup so that the
-// workgroups (<= 256) stay one per CU instead of doubling up on some CUs.
+// Other shapes between 256 and 512 tiles take two tiles per workgroup so that
+// the workgroups (<= 256) stay one per CU instead of doubling up on some CUs.
 struct NarrowConfig {
     int tww;      // tiles per workgroup: 1, 2 or 4
     int ksplit;   // waves per workgroup (octet ranges)
@@ -73,7 +77,7 @@ struct NarrowConfig {
 inline NarrowConfig narrow_config(const Geometry &g) {
     NarrowConfig c;
     int k;
-    if (g.tiles <= 256) {
+    if (g.tiles <= 256 || (g.tiles <= 512 && g.octets <= 2 * 16)) {
         c.tww = 1;
         k = 16;
     } else if (g.tiles <= 512 || g.tiles > 4096) {

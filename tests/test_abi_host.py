@@ -78,6 +78,11 @@ def test_workspace_bytes(lib):
     assert [nv.nvfp4_gemv_argmax_workspace_bytes(16, 32, n) for n in (0, 1, 4, 8, 9)] == [0, 32, 128, 256, 0]
     assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 4) == 4748 * 4 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 1) == 1088 * 8
+    # 257..512 tiles: one tile per workgroup while a row has at most 32
+    # octets (the 8192 x 4096 draft head), two tiles otherwise
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 4096, 1) == 512 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 5120, 1) == 256 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(5120, 17408, 1) == 160 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, 24, 4) == 0
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, (1 << 26) + 16, 4) == 0
 
