@@ -328,3 +328,31 @@ def test_wide_repeat_bit_identical(R, K, n):
     assert np.array_equal(codes[torch.as_tensor(rows, device=W.device)].cpu().numpy(), c_ref)
     Y_ref, S = oracle.gemv(c_ref, s_ref, 1.0, G.wl.bf16_bits(X))
     G.assert_within_tolerance(first.cpu().numpy()[:, rows], Y_ref, S, "wide repeat %dx%d n=%d" % (R, K, n))
+
+
+@pytest.mark.parametrize("R,K,n", [(8192, 4096, 1), (17408, 5120, 4), (2000, 1024, 8)])
+def test_matvec_repeat_bit_identical(R, K, n):
+    """Forty back-to-back launches of the matvec, and of its argmax form, give
+    the first launch's bits and row indices (the partial sums of a
+    workgroup's waves meet in LDS behind one barrier per launch)."""
+    W = G.seeded_matrix(R, K, 27)
+    codes, scales = G.quantize_gpu(W)
+    wq, ws = G.repack_gpu(codes, scales, R, K)
+    X = G.seeded_x(n, K, seed=28)
+    G.note("matvec repeat %dx%d n=%d" % (R, K, n))
+    first = G.gemv_gpu(wq, ws, 1.0, R, K, X)
+    logits0, am0 = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, X)
+    assert torch.equal(logits0.view(torch.int32), first.view(torch.int32))
+    Y = torch.empty_like(first)
+    logits = torch.empty_like(first)
+    am = torch.empty_like(am0)
+    wsp = torch.empty(nv.nvfp4_gemv_argmax_workspace_bytes(R, K, n), dtype=torch.uint8, device=G.DEV)
+    for i in range(40):
+        Y.fill_(float("nan"))
+        nv.nvfp4_gemv(wq, ws, 1.0, R, K, X, n, Y)
+        assert torch.equal(Y.view(torch.int32), first.view(torch.int32)), "launch %d differs" % i
+        logits.fill_(float("nan"))
+        am.fill_(-1)
+        nv.nvfp4_gemv_argmax(wq, ws, 1.0, R, K, X, n, logits, am, wsp)
+        assert torch.equal(logits.view(torch.int32), first.view(torch.int32)), "argmax launch %d differs" % i
+        assert torch.equal(am, am0), "argmax launch %d names other rows" % i
