@@ -315,6 +315,16 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const int cur = d & 1, nxt = cur ^ 1;
+            // A decoder wave decodes its slice of the next octet's extra
+            // tile here, between its own MFMAs, once that octet's weight
+            // loads (issued an octet earlier, ahead of the X loads and the
+            // first part of octet wo's) have landed.
+            if (d == 2 && EXTRA && xdecoder && o + 1 < octets) {
+                if (wo >= 0) __builtin_amdgcn_s_waitcnt(vmcnt_only(kXDmaPerWave + kWaveTiles));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_only(kXDmaPerWave));
+                asm volatile("" ::: "memory");   // the raw bytes' LDS reads stay below the wait
+                decode_extra(o + 1);
+            }
             if (d >= 1 && wo >= 0) load_w_part(wo, d - 1);
 #pragma unroll
             for (int cs = 0; cs < kWideSub; ++cs) {
@@ -344,10 +354,10 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
     // frees the buffers restaged next (read at octet o - 1).  A bare barrier:
     // __syncthreads() would also drain every outstanding load (its fence),
     // emptying the rings; the memory clobber keeps the LDS accesses on their
-    // side of it.  A decoder wave decodes octet o + 1's extra slice after
-    // octet o's MFMAs, once its own octet o + 1 weight loads (issued an octet
-    // earlier) are done.  The compiler barriers between the load groups keep
-    // the X and weight loads in program order, which the counts rely on.
+    // side of it.  A decoder wave decodes octet o + 1's extra slice in the
+    // middle of octet o's MFMAs (see compute), where its SIMD-mate's MFMAs
+    // hide it.  The compiler barriers between the load groups keep the X and
+    // weight loads in program order, which the counts rely on.
     auto fence = [] { asm volatile("" ::: "memory"); };
     auto run = [&](auto extra_c) {
         constexpr bool EXTRA = decltype(extra_c)::value;
@@ -375,12 +385,6 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
             if (o + 1 < octets) stage_x(o + 1);
             fence();
             compute(o, extra_c, o + 2 < octets ? o + 2 : -1);
-            if (decoder && o + 1 < octets) {
-                if (o + 2 < octets) __builtin_amdgcn_s_waitcnt(vmcnt_only(kXDmaPerWave + kWLoadsDec));
-                else __builtin_amdgcn_s_waitcnt(vmcnt_only(kXDmaPerWave));
-                fence();
-                decode_extra(o + 1);
-            }
         }
     };
     if (has_extra) run(std::true_type{});
