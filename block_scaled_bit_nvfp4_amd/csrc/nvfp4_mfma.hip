@@ -326,6 +326,14 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
                 decode_extra(o + 1);
             }
             if (d >= 1 && wo >= 0) load_w_part(wo, d - 1);
+            // Waves w and w + 4 share a SIMD, and at equal priority the older
+            // (w) wins the issue arbitration and ends its octet early, leaving
+            // w + 4 to finish alone.  w + 4 takes the higher priority for the
+            // first two slices, which brings the two to the barrier together.
+            if (wave >= kWideWaves / 2) {
+                if (d <= 1) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+            }
 #pragma unroll
             for (int cs = 0; cs < kWideSub; ++cs) {
 #pragma unroll
