@@ -106,8 +106,13 @@ __device__ __forceinline__ unsigned long long argmax_key(float y, uint32_t row) 
     return (static_cast<unsigned long long>(k) << 32) | (0xFFFFFFFFu - row);
 }
 
-template <int TWW>
-constexpr int scale_loads() { return TWW == 4 ? 1 : TWW; }
+// NVFP4 scale entries of a workgroup's tiles come in one 8-byte load per
+// lane when the tiles are two or four (lane 16 tt + r: row r of tile tt),
+// spread to the lane groups with permlane swaps; otherwise one per tile.
+template <int TWW, int FMT>
+constexpr bool merged_scales() { return TWW == 4 || (TWW == 2 && FMT == kNvfp4); }
+template <int TWW, int FMT>
+constexpr int scale_loads() { return merged_scales<TWW, FMT>() ? 1 : TWW; }
 
 // One octet of one wave's operands.  NVFP4 scale entries are 8 bytes per row
 // (the octet's eight 16-element blocks), MXFP4 ones 4 bytes (its four
@@ -118,7 +123,7 @@ using ScaleWord = typename std::conditional<FMT == kMxfp4, uint32_t, u32x2>::typ
 template <int NC, int TWW, int FMT = kNvfp4>
 struct OctetData {
     u32x4 code[TWW];                            // lane's 16-byte code entry of each tile
-    ScaleWord<FMT> scale[scale_loads<TWW>()];   // TWW == 4: lane 16tt + r holds tile tt row r; else row r of each tile
+    ScaleWord<FMT> scale[scale_loads<TWW, FMT>()];   // merged: lane 16tt + r holds tile tt row r; else row r of each tile
     u32x4 x[NC];                                // compact activations: lane 16c + 4p + q holds X[c][128o + 32p + 8q ..]
 };
 
@@ -145,7 +150,10 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
     const auto srs = make_rsrc(ws + st * octets * int64_t(SREGION), uint32_t(o1) * SREGION);
     const auto xrs = make_rsrc(X, uint32_t(N) * uint32_t(K) * 2u);
     const uint32_t coff = uint32_t(lane * 16 + tg * TWW * kCodeChunk);
-    const uint32_t soff = TWW == 4 ? uint32_t(lane * 8) : uint32_t((tg * TWW * kTileRows + r) * SROW);
+    const uint32_t soff = TWW == 4 ? uint32_t(lane * 8)
+                          : merged_scales<TWW, FMT>() ? (lane < TWW * kTileRows ? uint32_t((tg * TWW * kTileRows + lane) * SROW)
+                                                                               : kOutOfRange)
+                                                      : uint32_t((tg * TWW * kTileRows + r) * SROW);
 
     // Compact activation load of this lane: column xc (+4), k = 128o + 32xp + 8xq.
     const int xc = lane >> 4, xp = (lane >> 2) & 3, xq = lane & 3;
@@ -177,7 +185,7 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
         for (int tt = 0; tt < TWW; ++tt)
             d.code[tt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, co + tt * kCodeChunk, 0, kStream));
 #pragma unroll
-        for (int tt = 0; tt < scale_loads<TWW>(); ++tt) {
+        for (int tt = 0; tt < scale_loads<TWW, FMT>(); ++tt) {
             if constexpr (FMT == kMxfp4)
                 d.scale[tt] = __builtin_amdgcn_raw_buffer_load_b32(srs, so + tt * SCHUNK, 0, kStream);
             else
@@ -200,7 +208,7 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
         if constexpr (FMT == kMxfp4) {
 #pragma unroll
             for (int tt = 0; tt < TWW; ++tt) S[0][tt] = S[1][tt] = d.scale[tt];   // MX blocks 0..3
-        } else if (TWW == 4) {
+        } else if (merged_scales<TWW, FMT>()) {
             uint32_t t0[4], t1[4];
             gather_lane_groups(d.scale[0][0], t0);
             gather_lane_groups(d.scale[0][1], t1);
