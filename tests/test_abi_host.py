@@ -83,6 +83,9 @@ def test_workspace_bytes(lib):
     assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 4096, 1) == 512 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 5120, 1) == 256 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(5120, 17408, 1) == 160 * 8
+    # the two-tile parity shapes: 261 tiles with 33-octet rows, and 4100 tiles
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(4176, 4112, 1) == 66 * 2 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(65600, 528, 1) == 1025 * 2 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, 24, 4) == 0
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, (1 << 26) + 16, 4) == 0
 

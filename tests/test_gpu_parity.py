@@ -140,6 +140,12 @@ def _prepare(R, K, seed, outliers=True, tscale=1.0):
     (31, 96, 7, 1.0),
     (300, 17408, 8, 1.0),
     (16, 16, 1, 1.0),          # a single block
+    # two tiles per workgroup (257..512 tiles with rows over 32 octets, or
+    # over 4096 tiles), a ragged last octet and wave octet ranges that are no
+    # multiple of four: n = 1 takes the grouped activation/scale loads
+    (4176, 4112, 1, 1.0),
+    (4176, 4112, 2, 1.0),
+    (65600, 528, 1, 0.5),
 ])
 def test_gemv_parity(R, K, n, tscale):
     seed = 0 if (R, K) == (256, 512) else R + K
