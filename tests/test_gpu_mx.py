@@ -120,6 +120,9 @@ def test_mx_dequant_every_scale_byte_and_code(tscale):
     (256, 512, 1, 1.0), (100, 2080, 1, 1.0), (48, 3072, 2, 0.5), (129, 4096, 3, 1.0), (64, 5120, 4, 1.0),
     (40, 1024, 5, 2.0), (23, 1088, 6, 1.0), (31, 96, 7, 1.0), (300, 17408, 8, 1.0), (16, 32, 1, 1.0),
     (4096, 4096, 1, 1.0), (5120, 2048, 4, 1.0),
+    # two tiles per workgroup (261 tiles, 33-octet rows with a ragged last
+    # octet): n = 1 takes the grouped activation/scale loads
+    (4176, 4128, 1, 1.0), (4176, 4128, 3, 1.0),
 ])
 def test_mx_gemv_parity(R, K, n, tscale):
     wq, ws, c_ref, s_ref = _prepare(R, K, 21 + R + K, tscale)
