@@ -28,9 +28,10 @@
 // row's octets (8 blocks) over `ksplit` waves; each wave streams its octets
 // with range-checked buffer loads, one octet ahead of the MFMAs: per tile one
 // 16-byte code load (the tile's 1 KiB chunk), the scales of its rows, and one
-// compact 16-byte activation load per four columns.  Loads past the wave's
-// last octet read zeros with no memory traffic, so the loop needs no branch
-// around a load.
+// compact 16-byte activation load per four columns (for one column and
+// several tiles the activations and scales of four octets come in one load
+// each, a group ahead).  Loads past the wave's last octet read zeros with no
+// memory traffic, so the loop needs no branch around a load.
 //
 // A operands: the wave writes the octet's compact activations to its own LDS
 // slot and reads each A operand back with one ds_read_b128 per 32-k slice:
