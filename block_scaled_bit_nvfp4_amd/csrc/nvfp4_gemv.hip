@@ -211,7 +211,7 @@ int launch_narrow_tww(const Geometry &g, const NarrowConfig &cfg, const uint8_t 
 template <int MODE>
 int launch_narrow(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
                   int n, float *Y, unsigned long long *amax_ws, int32_t *argmax_out, hipStream_t stream) {
-    const NarrowConfig cfg = narrow_config(g);
+    const NarrowConfig cfg = narrow_config(g, n);
     switch (cfg.tww) {
         case 1: return launch_narrow_tww<MODE, 1>(g, cfg, wq, ws, tscale, X, n, Y, amax_ws, argmax_out, 0, nullptr,
                                                  cfg.ksplit, cfg.groups, stream);
@@ -226,10 +226,10 @@ int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float t
                 int n, float *Y, hipStream_t stream, int fmt = kNvfp4);
 
 // The MXFP4 matvec: the plain product's decomposition and kernel with the
-// E8M0 scale plane (the tile rule never picks four tiles per workgroup).
+// E8M0 scale plane, at most two tiles per workgroup.
 int launch_narrow_mx(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
                      int n, float *Y, hipStream_t stream) {
-    const NarrowConfig cfg = narrow_config(g);
+    const NarrowConfig cfg = narrow_config(g, n, 2);
     switch (cfg.tww) {
         case 1: return launch_narrow_tww<kPlain, 1, kMxfp4>(g, cfg, wq, ws, tscale, X, n, Y, nullptr, nullptr, 0,
                                                             nullptr, cfg.ksplit, cfg.groups, stream);
@@ -242,14 +242,14 @@ int launch_narrow_mx(const Geometry &g, const uint8_t *wq, const uint8_t *ws, fl
 // True when the fused gate||up+SwiGLU kernel reproduces the stacked product's
 // decomposition: the up rows start on a super-tile boundary and a workgroup
 // can hold both halves' waves.
-inline bool swiglu_fusable(const Geometry &stacked, int64_t F) {
-    return F % kSuperRows == 0 && 2 * narrow_config(stacked).ksplit <= kMaxKsplit;
+inline bool swiglu_fusable(const Geometry &stacked, int64_t F, int n) {
+    return F % kSuperRows == 0 && 2 * narrow_config(stacked, n).ksplit <= kMaxKsplit;
 }
 
 int launch_gemv_swiglu(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t hidden, int64_t F,
                        const uint16_t *X, int n, float *gu, uint16_t *h, hipStream_t stream) {
     const Geometry g(2 * F, hidden);
-    if (!swiglu_fusable(g, F)) {
+    if (!swiglu_fusable(g, F, n)) {
         // The plain product into gu, then the SwiGLU kernel: the same bits.
         if (!gu) return NVFP4_ESHAPE;
         if (int st = launch_narrow<kPlain>(g, wq, ws, tscale, X, n, gu, nullptr, nullptr, stream)) return st;
@@ -257,7 +257,7 @@ int launch_gemv_swiglu(const uint8_t *wq, const uint8_t *ws, float tscale, int64
                            F * n, h);
         return launch_status();
     }
-    const NarrowConfig cfg = narrow_config(g);
+    const NarrowConfig cfg = narrow_config(g, n);
     const int64_t groups = cfg.groups / 2;   // the gate half's workgroups
     const int up_st = int(F / kSuperRows);
     switch (cfg.tww) {
@@ -299,7 +299,7 @@ NVFP4_API int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int
 NVFP4_API size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, int n) {
     // One 64-bit key per workgroup and column.
     if (n < 1 || n > kMaxNarrowN || check_shape(rows, cols) != NVFP4_OK || cols > kMaxNarrowCols) return 0;
-    return size_t(narrow_config(Geometry(rows, cols)).groups) * size_t(n) * sizeof(unsigned long long);
+    return size_t(narrow_config(Geometry(rows, cols), n).groups) * size_t(n) * sizeof(unsigned long long);
 }
 
 NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
@@ -314,7 +314,7 @@ NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tsca
     (void)hipGetLastError();
     auto *keys = static_cast<unsigned long long *>(workspace);
     if (int st = launch_narrow<kArgmax>(g, wq, ws, tscale, X, n, logits, keys, argmax, stream)) return st;
-    const int groups = int(narrow_config(g).groups);
+    const int groups = int(narrow_config(g, n).groups);
 #define NVFP4_FINISH(NN) \
     hipLaunchKernelGGL(argmax_finish_kernel<NN>, dim3(1), dim3(kFinishThreads), 0, stream, keys, groups, argmax)
     switch (n) {

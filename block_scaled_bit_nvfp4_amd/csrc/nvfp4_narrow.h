@@ -53,11 +53,14 @@ constexpr int kMaxKsplit = 16;
 // activations of 8 columns stay below 2^31 bytes of buffer offset.
 constexpr int64_t kMaxNarrowCols = int64_t(1) << 26;
 
-// Decomposition of a rows x cols product over workgroups; a function of the
-// shape only.  Measured on the workload shapes (decode 4096 x 4096, the MLP's
+// Decomposition of a rows x cols product with n columns over workgroups.
+// The waves per workgroup (the octet ranges, hence every row's summation
+// order) are a function of the shape alone, so column c of an n-column
+// product has the bits of the 1-column product; the tiles per workgroup also
+// follow n.  Measured on the workload shapes (decode 4096 x 4096, the MLP's
 // 34816 x 5120 and 5120 x 17408, the 17408 x 5120 verify matrix, the
-// 151936 x 5120 vocabulary head and the 8192 x 4096 draft head) and on
-// 320..1024-tile sweeps at 4096 and 5120 columns: the narrow kernel keeps
+// 151936 x 5120 vocabulary head and the 8192 x 4096 draft head, n = 1..8) and
+// on 320..1024-tile sweeps at 4096 and 5120 columns: the narrow kernel keeps
 // enough bytes in flight with eight waves of two tiles per workgroup, except
 // that
 //   - small matrices (<= 256 tiles) want one tile per workgroup and sixteen
@@ -69,16 +72,24 @@ constexpr int64_t kMaxNarrowCols = int64_t(1) << 26;
 //     waves) at two workgroups per CU.
 // Other shapes between 256 and 512 tiles take two tiles per workgroup so that
 // the workgroups (<= 256) stay one per CU instead of doubling up on some CUs.
+// Past four columns a wave stages twice the activations per octet and runs
+// twice the block products per tile; a workgroup of more tiles spreads that
+// staging over more rows, so there the tiles per workgroup double (one to
+// two, two to four) except for small matrices and the two-tile shapes
+// between 256 and 512 tiles, where it leaves CUs idle: e.g. 8192 x 4096 at
+// n = 8 takes 7.2 instead of 8.4 us, the vocabulary head 74 instead of 83 us.
+// max_tww caps the tiles for kernels built only up to two (MXFP4).
 struct NarrowConfig {
     int tww;      // tiles per workgroup: 1, 2 or 4
     int ksplit;   // waves per workgroup (octet ranges)
     int64_t groups;   // workgroups
 };
 
-inline NarrowConfig narrow_config(const Geometry &g) {
+inline NarrowConfig narrow_config(const Geometry &g, int n, int max_tww = 4) {
     NarrowConfig c;
     int k;
-    if (g.tiles <= 256 || (g.tiles <= 512 && g.octets <= 2 * 16)) {
+    const bool small = g.tiles <= 256, short_rows = g.tiles <= 512 && g.octets <= 2 * 16;
+    if (small || short_rows) {
         c.tww = 1;
         k = 16;
     } else if (g.tiles <= 512 || g.tiles > 4096) {
@@ -88,6 +99,8 @@ inline NarrowConfig narrow_config(const Geometry &g) {
         c.tww = 1;
         k = 8;
     }
+    if (n > 4 && !small && (short_rows || g.tiles > 512)) c.tww *= 2;
+    if (c.tww > max_tww) c.tww = max_tww;
     if (k > g.octets) k = int(g.octets);
     c.ksplit = k < 1 ? 1 : k;
     c.groups = g.supertiles * (kSuperTiles / c.tww);

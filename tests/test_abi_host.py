@@ -86,6 +86,13 @@ def test_workspace_bytes(lib):
     # the two-tile parity shapes: 261 tiles with 33-octet rows, and 4100 tiles
     assert nv.nvfp4_gemv_argmax_workspace_bytes(4176, 4112, 1) == 66 * 2 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(65600, 528, 1) == 1025 * 2 * 8
+    # past four columns the tiles per workgroup double, except for small
+    # matrices and the two-tile shapes of 257..512 tiles
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 5) == 2374 * 5 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 8) == 544 * 8 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 4096, 6) == 256 * 6 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(4096, 4096, 8) == 256 * 8 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(5120, 17408, 8) == 160 * 8 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, 24, 4) == 0
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, (1 << 26) + 16, 4) == 0
 

@@ -40,7 +40,10 @@ NOT_FUSED = {(4096, 1024), (8192, 1024)}
 
 @pytest.mark.parametrize("D,F,n", [(512, 1024, 1), (1040, 2064, 2), (96, 48, 3), (5120, 17408, 1),
                                    (5120, 17408, 4), (4096, 1024, 8), (8192, 1024, 1), (8192, 1024, 2),
-                                   (1008, 1024, 5)])
+                                   (1008, 1024, 5),
+                                   # past four columns: two tiles per workgroup
+                                   # (520 stacked tiles), four (4104 tiles)
+                                   (1040, 4160, 6), (512, 32832, 5)])
 def test_gemv_swiglu_equals_two_launches(D, F, n):
     import block_scaled_bit_nvfp4_amd as nv
     _, q, ss = _stacked(D, F, seed=D + F)

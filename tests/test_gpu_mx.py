@@ -123,6 +123,9 @@ def test_mx_dequant_every_scale_byte_and_code(tscale):
     # two tiles per workgroup (261 tiles, 33-octet rows with a ragged last
     # octet): n = 1 takes the grouped activation/scale loads
     (4176, 4128, 1, 1.0), (4176, 4128, 3, 1.0),
+    # past four columns: two tiles per workgroup (261 tiles of 17-octet rows,
+    # 563 tiles); the cap at two (4102 tiles)
+    (4176, 2080, 5, 1.0), (9000, 1056, 8, 1.0), (65620, 544, 6, 1.0),
 ])
 def test_mx_gemv_parity(R, K, n, tscale):
     wq, ws, c_ref, s_ref = _prepare(R, K, 21 + R + K, tscale)
@@ -146,8 +149,8 @@ def test_mx_gemv_wide_parity(R, K, n):
     G.assert_within_tolerance(Y[:, rows], Y_ref, S, "mx gemv wide %dx%d n=%d" % (R, K, n))
 
 
-def test_mx_gemv_deterministic_and_column_identity():
-    R, K = 1040, 5120
+@pytest.mark.parametrize("R,K", [(1040, 5120), (9000, 1056)])
+def test_mx_gemv_deterministic_and_column_identity(R, K):
     wq, ws, _, _ = _prepare(R, K, 9)
     X = G.seeded_x(8, K, seed=10)
     G.note("mx gemv determinism")

@@ -146,6 +146,12 @@ def _prepare(R, K, seed, outliers=True, tscale=1.0):
     (4176, 4112, 1, 1.0),
     (4176, 4112, 2, 1.0),
     (65600, 528, 1, 0.5),
+    # past four columns the tiles per workgroup double: two for 261 tiles of
+    # 17-octet rows and for 563 tiles, four for 4102 tiles (ragged rows)
+    (4176, 2064, 7, 1.0),
+    (9000, 1040, 6, 1.0),
+    (65620, 528, 5, 1.0),
+    (65600, 528, 8, 0.5),
 ])
 def test_gemv_parity(R, K, n, tscale):
     seed = 0 if (R, K) == (256, 512) else R + K
@@ -198,8 +204,12 @@ def test_gemv_exact_special_cases():
         assert torch.equal(yj, y * 2.0**j)
 
 
-def test_gemv_deterministic_and_column_identity():
-    R, K = 1040, 5120
+@pytest.mark.parametrize("R,K", [
+    (1040, 5120),
+    # shapes whose tiles per workgroup change with the column count
+    (4176, 2064), (9000, 1040), (65620, 528),
+])
+def test_gemv_deterministic_and_column_identity(R, K):
     wq, ws, _, _ = _prepare(R, K, 9)
     X = G.seeded_x(8, K, seed=10)
     G.note("gemv determinism")
@@ -217,12 +227,15 @@ def test_gemv_deterministic_and_column_identity():
 
 # -------------------------------------------------------------- argmax, exact
 
-@pytest.mark.parametrize("n", [1, 4, 8])
-def test_argmax_matches_oracle(n):
-    R, K = 2000, 1024
-    wq, ws, c_ref, s_ref = _prepare(R, K, 11 + n)
+@pytest.mark.parametrize("R,K,n", [
+    (2000, 1024, 1), (2000, 1024, 4), (2000, 1024, 8),
+    # two and four tiles per workgroup past four columns
+    (9000, 1040, 6), (65620, 528, 5),
+])
+def test_argmax_matches_oracle(R, K, n):
+    wq, ws, c_ref, s_ref = _prepare(R, K, 11 + n + (0 if R == 2000 else R))
     X = G.seeded_x(n, K, seed=12)
-    G.note("argmax n=%d" % n)
+    G.note("argmax %dx%d n=%d" % (R, K, n))
     logits, am = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, X)
     Y_ref, S = oracle.gemv(c_ref, s_ref, 1.0, G.wl.bf16_bits(X))
     G.assert_within_tolerance(logits.cpu().numpy(), Y_ref, S, "argmax logits")
