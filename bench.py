@@ -119,19 +119,20 @@ class Step:
                     self.launches.append((self._swiglu(F), 1 * 2 * F * 4 + F * 2, 4 * F, "swiglu"))
                 self.launches.append((self._gemv(D, self.h, 1, self.y), gemv_bytes(D.rows, D.cols, 1),
                                       2 * D.rows * D.cols, "gemv"))
-        elif name == "verify_vocab_n4":
+        elif name in ("verify_vocab_n4", "verify_vocab_n8"):
             mw, head = w.matrices
-            self.x = wl.activations(4, mw.cols, seed=wl.seed_of(name, "x"), device=DEV)
+            n = w.n
+            self.x = wl.activations(n, mw.cols, seed=wl.seed_of(name, "x"), device=DEV)
             self.M1, self.M2 = Matrix(w, mw, 0), Matrix(w, head, 0)
-            self.y1 = torch.empty(4, mw.rows, dtype=torch.float32, device=DEV)
-            self.logits = torch.empty(4, head.rows, dtype=torch.float32, device=DEV)
-            self.am = torch.empty(4, dtype=torch.int32, device=DEV)
-            self.wsp = torch.empty(nv.nvfp4_gemv_argmax_workspace_bytes(head.rows, head.cols, 4), dtype=torch.uint8,
+            self.y1 = torch.empty(n, mw.rows, dtype=torch.float32, device=DEV)
+            self.logits = torch.empty(n, head.rows, dtype=torch.float32, device=DEV)
+            self.am = torch.empty(n, dtype=torch.int32, device=DEV)
+            self.wsp = torch.empty(nv.nvfp4_gemv_argmax_workspace_bytes(head.rows, head.cols, n), dtype=torch.uint8,
                                    device=DEV)
-            self.launches.append((self._gemv(self.M1, self.x, 4, self.y1), gemv_bytes(mw.rows, mw.cols, 4),
-                                  8 * mw.rows * mw.cols, "gemv"))
-            self.launches.append((self._argmax(), gemv_bytes(head.rows, head.cols, 4) + 4 * 4,
-                                  8 * head.rows * head.cols, "gemv"))
+            self.launches.append((self._gemv(self.M1, self.x, n, self.y1), gemv_bytes(mw.rows, mw.cols, n),
+                                  2 * n * mw.rows * mw.cols, "gemv"))
+            self.launches.append((self._argmax(), gemv_bytes(head.rows, head.cols, n) + 4 * n,
+                                  2 * n * head.rows * head.cols, "gemv"))
         elif name == "draft_head_8192x4096":
             m = w.matrices[0]
             self.x = wl.activations(1, m.cols, seed=wl.seed_of(name, "x"), device=DEV)
@@ -187,7 +188,8 @@ class Step:
         M = self.M2
 
         def f():
-            nv.nvfp4_gemv_argmax(M.wq, M.ws, M.tscale, M.rows, M.cols, self.x, 4, self.logits, self.am, self.wsp)
+            nv.nvfp4_gemv_argmax(M.wq, M.ws, M.tscale, M.rows, M.cols, self.x, self.n, self.logits, self.am,
+                                 self.wsp)
         return f
 
     def _argmax_of(self, M, logits, am):
@@ -250,7 +252,7 @@ def cpu_baseline(step, budget_s=12.0, min_s=10.0):
     elif w.name == "mlp_27b_decode":
         for G_, D in step.layers:
             sample.append((G_, step.x, None))
-    elif w.name == "verify_vocab_n4":
+    elif w.name in ("verify_vocab_n4", "verify_vocab_n8"):
         sample.append((step.M1, step.x, None))
         sample.append((step.M2, step.x, np.arange(0, step.M2.rows, 8)))
     elif w.name in ("prefill_n512", "mxfp4_prefill_n512"):

@@ -65,6 +65,12 @@ WORKLOADS = {
         "with per-column argmax",
         4, (Matrix("w", 17408, 5120), Matrix("lm_head", 151936, 5120)), copies=1,
         argmax=("lm_head",)),
+    # The widest verify the matvec takes: seven drafted tokens plus one.
+    "verify_vocab_n8": Workload(
+        "verify_vocab_n8", "speculative verify N=8: 17408x5120 and lm_head 151936x5120 "
+        "with per-column argmax",
+        8, (Matrix("w", 17408, 5120), Matrix("lm_head", 151936, 5120)), copies=1,
+        argmax=("lm_head",)),
     # The N = 512 contraction runs over four layer copies per step, so that a
     # step's launches run back to back as a prefill's layers would.
     "prefill_n512": Workload(

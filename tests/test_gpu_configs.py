@@ -105,12 +105,14 @@ def test_mlp_27b_decode_layer():
     G.assert_within_tolerance(y, Y2, S2, "mlp down")
 
 
-def test_verify_vocab_n4_with_full_argmax():
-    w = wl.WORKLOADS["verify_vocab_n4"]
+@pytest.mark.parametrize("name", ["verify_vocab_n4", "verify_vocab_n8"])
+def test_verify_vocab_with_full_argmax(name):
+    w = wl.WORKLOADS[name]
     mw, head = w.matrices
-    X = wl.activations(4, mw.cols, seed=wl.seed_of(w.name, "x"), device=G.DEV)
+    n = w.n
+    X = wl.activations(n, mw.cols, seed=wl.seed_of(w.name, "x"), device=G.DEV)
     xb = wl.bf16_bits(X)
-    G.note("config verify_vocab_n4 w")
+    G.note("config %s w" % name)
     W1, c1, s1, q1, ss1 = _matrix(w, mw)
     Y1 = G.gemv_gpu(q1, ss1, w.tscale, mw.rows, mw.cols, X).cpu().numpy()
     rows = _sample_rows(mw.rows, 512, 2)
@@ -118,12 +120,12 @@ def test_verify_vocab_n4_with_full_argmax():
     Yr, S = oracle.gemv_rows(c_ref, s_ref, w.tscale, xb)
     G.assert_within_tolerance(Y1[:, rows], Yr, S, "verify w")
     # column identity with N=1 on the same matrix
-    for c in range(4):
+    for c in range(n):
         y1 = G.gemv_gpu(q1, ss1, w.tscale, mw.rows, mw.cols, X[c:c + 1].contiguous()).cpu().numpy()
         assert np.array_equal(y1[0].view(np.uint32), Y1[c].view(np.uint32))
     del W1
     torch.cuda.empty_cache()
-    G.note("config verify_vocab_n4 lm_head")
+    G.note("config %s lm_head" % name)
     W2, c2, s2, q2, ss2 = _matrix(w, head)
     logits, am = G.gemv_argmax_gpu(q2, ss2, w.tscale, head.rows, head.cols, X)
     W2h = W2.cpu().numpy()
@@ -138,7 +140,7 @@ def test_verify_vocab_n4_with_full_argmax():
     want = oracle.argmax_first(Y2)
     assert list(am.cpu().numpy()) == list(want)
     # report how far the winner leads the runner-up next to the tolerance
-    for c in range(4):
+    for c in range(n):
         order = np.argsort(Y2[c])
         margin = Y2[c][order[-1]] - Y2[c][order[-2]]
         bound = 1e-5 * (S2[c][order[-1]] + S2[c][order[-2]]) + 2e-6

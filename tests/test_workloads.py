@@ -7,7 +7,7 @@ from block_scaled_bit_nvfp4_amd import workloads as wl
 
 def test_workload_table():
     assert set(wl.WORKLOADS) == {"gemv_256x512", "decode_4096x4096", "mlp_27b_decode",
-                                 "verify_vocab_n4", "prefill_n512", "draft_head_8192x4096",
+                                 "verify_vocab_n4", "verify_vocab_n8", "prefill_n512", "draft_head_8192x4096",
                                  "mxfp4_gemv_17408x5120", "mxfp4_prefill_n512"}
     assert wl.WORKLOADS["mxfp4_prefill_n512"].fmt == "mxfp4"
     assert wl.WORKLOADS["prefill_n512"].fmt == "nvfp4"
@@ -17,6 +17,8 @@ def test_workload_table():
     m = wl.WORKLOADS["mlp_27b_decode"].matrices
     assert (m[0].rows, m[0].cols, m[1].rows, m[1].cols) == (34816, 5120, 5120, 17408)
     assert wl.WORKLOADS["verify_vocab_n4"].n == 4
+    assert wl.WORKLOADS["verify_vocab_n8"].n == 8
+    assert wl.WORKLOADS["verify_vocab_n8"].matrices == wl.WORKLOADS["verify_vocab_n4"].matrices
     assert wl.WORKLOADS["prefill_n512"].n == 512
     assert wl.seed_of("gemv_256x512", "w") == 0
     assert wl.seed_of("decode_4096x4096", "w", 1) != wl.seed_of("decode_4096x4096", "w", 2)
