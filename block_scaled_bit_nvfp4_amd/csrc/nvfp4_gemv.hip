@@ -113,9 +113,16 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
     // a multiple of 64 and SEG divides 64, so a segment never straddles a
     // wave or an iteration.
     for (int idx = threadIdx.x; idx < N * SEG; idx += blockDim.x) {
+        // every wave's partial is read before the first add (clamped indices,
+        // adds in wave order): one LDS round trip instead of one per batch
         const int c = idx / SEG, lr = idx % SEG;
-        float tot = red[c * SEG + lr];
-        for (int w = 1; w < ksplit; ++w) tot += red[(w * N + c) * SEG + lr];
+        float part[kMaxKsplit];
+#pragma unroll
+        for (int w = 0; w < kMaxKsplit; ++w) part[w] = red[((w < ksplit ? w : 0) * N + c) * SEG + lr];
+        float tot = part[0];
+#pragma unroll
+        for (int w = 1; w < kMaxKsplit; ++w)
+            if (w < ksplit) tot += part[w];
         const float y = tot * tscale;
         const int row = row0 + lr;
         const bool valid = row < rows;
