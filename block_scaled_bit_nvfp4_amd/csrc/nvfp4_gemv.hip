@@ -91,12 +91,24 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
     if (MODE == kSwiglu) {
         const int F = up_st * kSuperRows;
         for (int idx = threadIdx.x; idx < N * SEG; idx += blockDim.x) {
+            // both halves' partials read before the first add (at most
+            // kMaxKsplit / 2 waves per half), adds in wave order
+            constexpr int KH = kMaxKsplit / 2;
             const int c = idx / SEG, lr = idx % SEG;
-            float gs = red[c * SEG + lr], us = red[(ksplit * N + c) * SEG + lr];
-            for (int w = 1; w < ksplit; ++w) {
-                gs += red[(w * N + c) * SEG + lr];
-                us += red[((ksplit + w) * N + c) * SEG + lr];
+            float gp[KH], up[KH];
+#pragma unroll
+            for (int w = 0; w < KH; ++w) {
+                const int ww = w < ksplit ? w : 0;
+                gp[w] = red[(ww * N + c) * SEG + lr];
+                up[w] = red[((ksplit + ww) * N + c) * SEG + lr];
             }
+            float gs = gp[0], us = up[0];
+#pragma unroll
+            for (int w = 1; w < KH; ++w)
+                if (w < ksplit) {
+                    gs += gp[w];
+                    us += up[w];
+                }
             gs *= tscale;
             us *= tscale;
             const int row = row0 + lr;
