@@ -108,6 +108,46 @@ __device__ __forceinline__ bf16x8 e2m1x8_bf16_e8m0(uint32_t word, uint32_t b) {
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
 __device__ __forceinline__ uint32_t as_u32(bf16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// One DPP step of a 64-bit maximum: each lane takes the larger of its value
+// and the value of the lane CTRL names (quad permutation or row mirror).
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max_u64(unsigned long long v) {
+    const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(v)), CTRL, 0xF, 0xF, false));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(v >> 32)), CTRL, 0xF, 0xF, false));
+    const unsigned long long o = (static_cast<unsigned long long>(hi) << 32) | lo;
+    return o > v ? o : v;
+}
+
+// Maximum of a 64-bit value over each aligned group of G lanes (G = 16, 32 or
+// 64), left in every lane of the group, without LDS: quad swaps, then the
+// half-row and row mirrors (16 lanes), then permlane swaps across rows.
+// Every lane of a group must be active.
+template <int G>
+__device__ __forceinline__ unsigned long long lanes_max_u64(unsigned long long v) {
+    static_assert(G == 16 || G == 32 || G == 64, "lane group of 16, 32 or 64");
+    v = dpp_max_u64<0xB1>(v);    // quad_perm [1,0,3,2]
+    v = dpp_max_u64<0x4E>(v);    // quad_perm [2,3,0,1]
+    v = dpp_max_u64<0x141>(v);   // row_half_mirror: quads 0|1 and 2|3 of a row
+    v = dpp_max_u64<0x140>(v);   // row_mirror: the two halves of a row
+    if constexpr (G >= 32) {
+        // rows (x0 x1 x2 x3) -> (x0 x0 x2 x2) and (x1 x1 x3 x3)
+        const auto l = __builtin_amdgcn_permlane16_swap(uint32_t(v), uint32_t(v), false, false);
+        const auto h = __builtin_amdgcn_permlane16_swap(uint32_t(v >> 32), uint32_t(v >> 32), false, false);
+        const unsigned long long a = (static_cast<unsigned long long>(h[0]) << 32) | l[0];
+        const unsigned long long b = (static_cast<unsigned long long>(h[1]) << 32) | l[1];
+        v = a > b ? a : b;
+    }
+    if constexpr (G == 64) {
+        // (y0 y1 y2 y3) -> (y0 y1 y0 y1) and (y2 y3 y2 y3)
+        const auto l = __builtin_amdgcn_permlane32_swap(uint32_t(v), uint32_t(v), false, false);
+        const auto h = __builtin_amdgcn_permlane32_swap(uint32_t(v >> 32), uint32_t(v >> 32), false, false);
+        const unsigned long long a = (static_cast<unsigned long long>(h[0]) << 32) | l[0];
+        const unsigned long long b = (static_cast<unsigned long long>(h[1]) << 32) | l[1];
+        v = a > b ? a : b;
+    }
+    return v;
+}
+
 // v holds item g in lane group g (lanes 16g .. 16g + 15); returns o[k] = item
 // k in every lane.  One v_permlane32_swap and two v_permlane16_swap.
 __device__ __forceinline__ void gather_lane_groups(uint32_t v, uint32_t (&o)[4]) {

@@ -140,12 +140,8 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
         const bool valid = row < rows;
         if (valid && Y) Y[int64_t(c) * rows + row] = y;
         if (MODE == kArgmax) {
-            unsigned long long key = valid ? argmax_key(y, uint32_t(row)) : 0ull;
-#pragma unroll
-            for (int o = SEG / 2; o >= 1; o >>= 1) {
-                const unsigned long long other = __shfl_xor(key, o);
-                key = other > key ? other : key;
-            }
+            // the segment's SEG lanes are all active (SEG divides 64)
+            const unsigned long long key = lanes_max_u64<SEG>(valid ? argmax_key(y, uint32_t(row)) : 0ull);
             if (lr == 0) amax_ws[int64_t(blockIdx.x) * N + c] = key;
         }
     }
@@ -220,11 +216,7 @@ argmax_finish_kernel(const unsigned long long *__restrict__ keys, int groups, in
     }
 #pragma unroll
     for (int c = 0; c < N; ++c) {
-#pragma unroll
-        for (int o = kLanes / 2; o >= 1; o >>= 1) {
-            const unsigned long long other = __shfl_xor(m[c], o);
-            m[c] = other > m[c] ? other : m[c];
-        }
+        m[c] = lanes_max_u64<kLanes>(m[c]);
         if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][c] = m[c];
     }
     __syncthreads();
