@@ -118,6 +118,29 @@ __device__ __forceinline__ unsigned long long dpp_max_u64(unsigned long long v) 
     return o > v ? o : v;
 }
 
+// Maximum of a 64-bit value over the rows (16-lane groups) of each aligned
+// group of G lanes (G = 32 or 64), for values already reduced within rows
+// (or per lane class): permlane swaps, no LDS.
+template <int G>
+__device__ __forceinline__ unsigned long long rows_max_u64(unsigned long long v) {
+    static_assert(G == 32 || G == 64, "row group of 32 or 64 lanes");
+    // rows (x0 x1 x2 x3) -> (x0 x0 x2 x2) and (x1 x1 x3 x3)
+    const auto l = __builtin_amdgcn_permlane16_swap(uint32_t(v), uint32_t(v), false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(uint32_t(v >> 32), uint32_t(v >> 32), false, false);
+    unsigned long long a = (static_cast<unsigned long long>(h[0]) << 32) | l[0];
+    unsigned long long b = (static_cast<unsigned long long>(h[1]) << 32) | l[1];
+    v = a > b ? a : b;
+    if constexpr (G == 64) {
+        // (y0 y1 y2 y3) -> (y0 y1 y0 y1) and (y2 y3 y2 y3)
+        const auto l2 = __builtin_amdgcn_permlane32_swap(uint32_t(v), uint32_t(v), false, false);
+        const auto h2 = __builtin_amdgcn_permlane32_swap(uint32_t(v >> 32), uint32_t(v >> 32), false, false);
+        a = (static_cast<unsigned long long>(h2[0]) << 32) | l2[0];
+        b = (static_cast<unsigned long long>(h2[1]) << 32) | l2[1];
+        v = a > b ? a : b;
+    }
+    return v;
+}
+
 // Maximum of a 64-bit value over each aligned group of G lanes (G = 16, 32 or
 // 64), left in every lane of the group, without LDS: quad swaps, then the
 // half-row and row mirrors (16 lanes), then permlane swaps across rows.
@@ -129,22 +152,7 @@ __device__ __forceinline__ unsigned long long lanes_max_u64(unsigned long long v
     v = dpp_max_u64<0x4E>(v);    // quad_perm [2,3,0,1]
     v = dpp_max_u64<0x141>(v);   // row_half_mirror: quads 0|1 and 2|3 of a row
     v = dpp_max_u64<0x140>(v);   // row_mirror: the two halves of a row
-    if constexpr (G >= 32) {
-        // rows (x0 x1 x2 x3) -> (x0 x0 x2 x2) and (x1 x1 x3 x3)
-        const auto l = __builtin_amdgcn_permlane16_swap(uint32_t(v), uint32_t(v), false, false);
-        const auto h = __builtin_amdgcn_permlane16_swap(uint32_t(v >> 32), uint32_t(v >> 32), false, false);
-        const unsigned long long a = (static_cast<unsigned long long>(h[0]) << 32) | l[0];
-        const unsigned long long b = (static_cast<unsigned long long>(h[1]) << 32) | l[1];
-        v = a > b ? a : b;
-    }
-    if constexpr (G == 64) {
-        // (y0 y1 y2 y3) -> (y0 y1 y0 y1) and (y2 y3 y2 y3)
-        const auto l = __builtin_amdgcn_permlane32_swap(uint32_t(v), uint32_t(v), false, false);
-        const auto h = __builtin_amdgcn_permlane32_swap(uint32_t(v >> 32), uint32_t(v >> 32), false, false);
-        const unsigned long long a = (static_cast<unsigned long long>(h[0]) << 32) | l[0];
-        const unsigned long long b = (static_cast<unsigned long long>(h[1]) << 32) | l[1];
-        v = a > b ? a : b;
-    }
+    if constexpr (G >= 32) v = rows_max_u64<G>(v);
     return v;
 }
 

@@ -180,12 +180,9 @@ argmax_finish_kernel(const unsigned long long *__restrict__ keys, int groups, in
 #pragma unroll
             for (int u = 0; u < U; ++u) m = k[u] > m ? k[u] : m;
         }
-        // lanes l and l ^ o share a column for every o >= N
-#pragma unroll
-        for (int o = kLanes / 2; o >= N; o >>= 1) {
-            const unsigned long long other = __shfl_xor(m, o);
-            m = other > m ? other : m;
-        }
+        // lanes l, l ^ 8, l ^ 16 and l ^ 32 share a column: row_ror:8 pairs
+        // lane i of a row with lane i ^ 8, then the rows meet by permlanes
+        m = rows_max_u64<kLanes>(dpp_max_u64<0x128>(m));
         if ((threadIdx.x & 63) < N) part[threadIdx.x >> 6][threadIdx.x & 63] = m;
         __syncthreads();
         if (threadIdx.x < N) {
