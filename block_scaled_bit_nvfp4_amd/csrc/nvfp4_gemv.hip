@@ -55,8 +55,7 @@ template <int N, int TWW, int MODE, int FMT = kNvfp4>
 __global__ void __launch_bounds__(kLanes * kMaxKsplit)
 narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows, int octets,
               int kb, int ksplit, const uint16_t *__restrict__ X, int K, float *__restrict__ Y,
-              unsigned long long *__restrict__ amax_ws, int32_t *__restrict__ argmax_out, int up_st,
-              uint16_t *__restrict__ h) {
+              unsigned long long *__restrict__ amax_ws, int up_st, uint16_t *__restrict__ h) {
     // [waves][narrow_wave_lds_bytes(N)] activation slots, then the partial
     // sums [waves][N][SEG]
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -231,13 +230,13 @@ argmax_finish_kernel(const unsigned long long *__restrict__ keys, int groups, in
 template <int MODE, int TWW, int FMT = kNvfp4>
 int launch_narrow_tww(const Geometry &g, const NarrowConfig &cfg, const uint8_t *wq, const uint8_t *ws,
                       float tscale, const uint16_t *X, int n, float *Y, unsigned long long *amax_ws,
-                      int32_t *argmax_out, int up_st, uint16_t *h, int waves, int64_t groups, hipStream_t stream) {
+                      int up_st, uint16_t *h, int waves, int64_t groups, hipStream_t stream) {
     const dim3 grid{unsigned(groups)}, block{unsigned(kLanes * waves)};
     const size_t lds = size_t(waves) * (size_t(narrow_wave_lds_bytes(n)) + size_t(n) * TWW * kTileRows * sizeof(float));
     const int rows = int(g.rows), octets = int(g.octets), kb = int(g.kb), K = int(g.cols);
 #define NVFP4_LAUNCH(NN)                                                                                      \
     hipLaunchKernelGGL((narrow_kernel<NN, TWW, MODE, FMT>), grid, block, lds, stream, wq, ws, tscale, rows, octets, \
-                       kb, cfg.ksplit, X, K, Y, amax_ws, argmax_out, up_st, h)
+                       kb, cfg.ksplit, X, K, Y, amax_ws, up_st, h)
     switch (n) {
         case 1: NVFP4_LAUNCH(1); break;
         case 2: NVFP4_LAUNCH(2); break;
@@ -255,15 +254,15 @@ int launch_narrow_tww(const Geometry &g, const NarrowConfig &cfg, const uint8_t 
 
 template <int MODE>
 int launch_narrow(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
-                  int n, float *Y, unsigned long long *amax_ws, int32_t *argmax_out, hipStream_t stream) {
+                  int n, float *Y, unsigned long long *amax_ws, hipStream_t stream) {
     const NarrowConfig cfg = narrow_config(g, n);
     switch (cfg.tww) {
-        case 1: return launch_narrow_tww<MODE, 1>(g, cfg, wq, ws, tscale, X, n, Y, amax_ws, argmax_out, 0, nullptr,
-                                                 cfg.ksplit, cfg.groups, stream);
-        case 2: return launch_narrow_tww<MODE, 2>(g, cfg, wq, ws, tscale, X, n, Y, amax_ws, argmax_out, 0, nullptr,
-                                                 cfg.ksplit, cfg.groups, stream);
-        default: return launch_narrow_tww<MODE, 4>(g, cfg, wq, ws, tscale, X, n, Y, amax_ws, argmax_out, 0,
-                                                  nullptr, cfg.ksplit, cfg.groups, stream);
+        case 1: return launch_narrow_tww<MODE, 1>(g, cfg, wq, ws, tscale, X, n, Y, amax_ws, 0, nullptr, cfg.ksplit,
+                                                 cfg.groups, stream);
+        case 2: return launch_narrow_tww<MODE, 2>(g, cfg, wq, ws, tscale, X, n, Y, amax_ws, 0, nullptr, cfg.ksplit,
+                                                 cfg.groups, stream);
+        default: return launch_narrow_tww<MODE, 4>(g, cfg, wq, ws, tscale, X, n, Y, amax_ws, 0, nullptr,
+                                                  cfg.ksplit, cfg.groups, stream);
     }
 }
 
@@ -276,10 +275,10 @@ int launch_narrow_mx(const Geometry &g, const uint8_t *wq, const uint8_t *ws, fl
                      int n, float *Y, hipStream_t stream) {
     const NarrowConfig cfg = narrow_config(g, n, 2);
     switch (cfg.tww) {
-        case 1: return launch_narrow_tww<kPlain, 1, kMxfp4>(g, cfg, wq, ws, tscale, X, n, Y, nullptr, nullptr, 0,
-                                                            nullptr, cfg.ksplit, cfg.groups, stream);
-        case 2: return launch_narrow_tww<kPlain, 2, kMxfp4>(g, cfg, wq, ws, tscale, X, n, Y, nullptr, nullptr, 0,
-                                                            nullptr, cfg.ksplit, cfg.groups, stream);
+        case 1: return launch_narrow_tww<kPlain, 1, kMxfp4>(g, cfg, wq, ws, tscale, X, n, Y, nullptr, 0, nullptr,
+                                                            cfg.ksplit, cfg.groups, stream);
+        case 2: return launch_narrow_tww<kPlain, 2, kMxfp4>(g, cfg, wq, ws, tscale, X, n, Y, nullptr, 0, nullptr,
+                                                            cfg.ksplit, cfg.groups, stream);
         default: return NVFP4_EINVAL;
     }
 }
@@ -297,7 +296,7 @@ int launch_gemv_swiglu(const uint8_t *wq, const uint8_t *ws, float tscale, int64
     if (!swiglu_fusable(g, F, n)) {
         // The plain product into gu, then the SwiGLU kernel: the same bits.
         if (!gu) return NVFP4_ESHAPE;
-        if (int st = launch_narrow<kPlain>(g, wq, ws, tscale, X, n, gu, nullptr, nullptr, stream)) return st;
+        if (int st = launch_narrow<kPlain>(g, wq, ws, tscale, X, n, gu, nullptr, stream)) return st;
         hipLaunchKernelGGL(swiglu_kernel, dim3(unsigned(ceil_div(F * n, 256))), dim3(256), 0, stream, gu, F,
                            F * n, h);
         return launch_status();
@@ -306,12 +305,12 @@ int launch_gemv_swiglu(const uint8_t *wq, const uint8_t *ws, float tscale, int64
     const int64_t groups = cfg.groups / 2;   // the gate half's workgroups
     const int up_st = int(F / kSuperRows);
     switch (cfg.tww) {
-        case 1: return launch_narrow_tww<kSwiglu, 1>(g, cfg, wq, ws, tscale, X, n, gu, nullptr, nullptr, up_st, h,
+        case 1: return launch_narrow_tww<kSwiglu, 1>(g, cfg, wq, ws, tscale, X, n, gu, nullptr, up_st, h,
                                                     2 * cfg.ksplit, groups, stream);
-        case 2: return launch_narrow_tww<kSwiglu, 2>(g, cfg, wq, ws, tscale, X, n, gu, nullptr, nullptr, up_st, h,
+        case 2: return launch_narrow_tww<kSwiglu, 2>(g, cfg, wq, ws, tscale, X, n, gu, nullptr, up_st, h,
                                                     2 * cfg.ksplit, groups, stream);
-        default: return launch_narrow_tww<kSwiglu, 4>(g, cfg, wq, ws, tscale, X, n, gu, nullptr, nullptr, up_st,
-                                                     h, 2 * cfg.ksplit, groups, stream);
+        default: return launch_narrow_tww<kSwiglu, 4>(g, cfg, wq, ws, tscale, X, n, gu, nullptr, up_st, h,
+                                                     2 * cfg.ksplit, groups, stream);
     }
 }
 
@@ -337,7 +336,7 @@ NVFP4_API int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int
     if (!aligned(Y, 4)) return NVFP4_EALIGN;
     const Geometry g(rows, cols);
     (void)hipGetLastError();
-    if (n <= kMaxNarrowN) return launch_narrow<kPlain>(g, wq, ws, tscale, X, n, Y, nullptr, nullptr, stream);
+    if (n <= kMaxNarrowN) return launch_narrow<kPlain>(g, wq, ws, tscale, X, n, Y, nullptr, stream);
     return launch_mfma(g, wq, ws, tscale, X, n, Y, stream);
 }
 
@@ -358,7 +357,7 @@ NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tsca
     const Geometry g(rows, cols);
     (void)hipGetLastError();
     auto *keys = static_cast<unsigned long long *>(workspace);
-    if (int st = launch_narrow<kArgmax>(g, wq, ws, tscale, X, n, logits, keys, argmax, stream)) return st;
+    if (int st = launch_narrow<kArgmax>(g, wq, ws, tscale, X, n, logits, keys, stream)) return st;
     const int groups = int(narrow_config(g, n).groups);
 #define NVFP4_FINISH(NN) \
     hipLaunchKernelGGL(argmax_finish_kernel<NN>, dim3(1), dim3(kFinishThreads), 0, stream, keys, groups, argmax)
