@@ -231,6 +231,9 @@ def test_gemv_deterministic_and_column_identity(R, K):
     (2000, 1024, 1), (2000, 1024, 4), (2000, 1024, 8),
     # two and four tiles per workgroup past four columns
     (9000, 1040, 6), (65620, 528, 5),
+    # 4219..8438 workgroups: the finish kernel takes two passes over the keys
+    # (per-group loads at n = 1 and 5, the one-column-per-thread loads at 8)
+    (270000, 16, 1), (270000, 16, 5), (270000, 16, 8),
 ])
 def test_argmax_matches_oracle(R, K, n):
     wq, ws, c_ref, s_ref = _prepare(R, K, 11 + n + (0 if R == 2000 else R))
