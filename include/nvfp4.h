@@ -139,7 +139,8 @@ int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
 
 /* Workspace bytes nvfp4_gemv_argmax needs for a rows x cols matrix and n
  * columns: one 64-bit key per workgroup of the product and column (at most
- * 4 * rows bytes); 0 for an invalid shape or n out of 1..8. */
+ * 4 bytes per row, rows rounded up to a multiple of 64); 0 for an invalid
+ * shape or n out of 1..8. */
 size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, int n);
 
 /* nvfp4_gemv for 1 <= n <= 8 plus, per column c, argmax[c] = the lowest row

@@ -94,6 +94,10 @@ def test_workspace_bytes(lib):
     assert nv.nvfp4_gemv_argmax_workspace_bytes(4096, 4096, 8) == 256 * 8 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(5120, 17408, 8) == 160 * 8 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, 24, 4) == 0
+    # the bound the header states: 4 bytes per row, rows rounded up to 64
+    for R, K in ((1, 16), (16, 32), (65, 512), (4176, 2064), (65620, 528), (151936, 5120)):
+        for n in range(1, 9):
+            assert 0 < nv.nvfp4_gemv_argmax_workspace_bytes(R, K, n) <= 4 * (-(-R // 64) * 64), (R, K, n)
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, (1 << 26) + 16, 4) == 0
 
 
