@@ -56,7 +56,11 @@
  *     the host, kernels are enqueued on `stream`, and the call returns
  *     without waiting.  No host synchronisation, no device allocation.
  *   - Pointers to weights, activations and fp32 matrices must be 16-byte
- *     aligned (NVFP4_EALIGN otherwise); row lengths follow from cols % 16.
+ *     aligned (NVFP4_EALIGN otherwise).
+ *   - NVFP4 rows are any whole number of 16-element blocks (cols % 16 == 0,
+ *     MXFP4: cols % 32 == 0): the repacked planes zero-pad the last octet,
+ *     and every kernel range-checks its activation loads, so no row length
+ *     beyond whole scale blocks is required.
  *   - Activations X are bf16 bit patterns [n][cols] row-major; outputs Y are
  *     fp32 [n][rows] row-major (column c of the product is X[c], Y[c]).
  *   - Return value: NVFP4_OK or a negative NVFP4_E* code; nvfp4_strerror
@@ -140,7 +144,10 @@ int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
 /* Workspace bytes nvfp4_gemv_argmax needs for a rows x cols matrix and n
  * columns: one 64-bit key per workgroup of the product and column (at most
  * 4 bytes per row, rows rounded up to a multiple of 64); 0 for an invalid
- * shape or n out of 1..8. */
+ * shape or n out of 1..8.  It takes the matrix shape as well as n because
+ * the product's workgroup count follows the shape; a caller that sizes one
+ * workspace for every call of a model uses its largest matrix and n = 8
+ * (4 bytes per row bound that for every n). */
 size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, int n);
 
 /* nvfp4_gemv for 1 <= n <= 8 plus, per column c, argmax[c] = the lowest row
@@ -221,7 +228,12 @@ int mxfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t ro
  * each 32-element block's dot product on MFMA and its scale in fp32; larger
  * n the dequant-to-bf16 MFMA contraction, decoding with one scaled
  * conversion per two elements), the same fixed summation order and column
- * identity. */
+ * identity.  Domain: the sums run in fp32 (the wide product's decoded
+ * weights in bf16, the same exponent range) before the tensor scale, so a
+ * weight whose e2m1 * 2^(b - 127) passes fp32's range (scale bytes 253 and
+ * 254 with |e2m1| >= 4 resp. >= 2) makes its outputs infinite or NaN even
+ * where tscale < 1 would bring the exact result back into range.  Subnormal
+ * scales (bytes 0 and 1) are exact in both products. */
 int mxfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
                const uint16_t *X, int n, float *Y, hipStream_t stream);
 

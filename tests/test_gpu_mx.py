@@ -149,21 +149,28 @@ def test_mx_gemv_wide_parity(R, K, n):
     G.assert_within_tolerance(Y[:, rows], Y_ref, S, "mx gemv wide %dx%d n=%d" % (R, K, n))
 
 
-@pytest.mark.parametrize("R,K", [(1040, 5120), (9000, 1056)])
+@pytest.mark.parametrize("R,K", [
+    (1040, 5120),
+    # tiles per workgroup change with the column count: 261 tiles of
+    # 17-octet rows and 563 tiles (one tile, two past four columns)
+    (4176, 2080), (9000, 1056),
+])
 def test_mx_gemv_deterministic_and_column_identity(R, K):
+    """Every width n = 1..8 gives, in column c, the bits of the one-column
+    product of X[c], and the same bits on a second launch."""
     wq, ws, _, _ = _prepare(R, K, 9)
     X = G.seeded_x(8, K, seed=10)
-    G.note("mx gemv determinism")
-    ys = {}
-    for n in (1, 2, 4, 8):
-        ys[n] = mx_gemv_gpu(wq, ws, 1.0, R, K, X[:n].contiguous())
-        again = mx_gemv_gpu(wq, ws, 1.0, R, K, X[:n].contiguous())
-        assert torch.equal(ys[n].view(torch.int32), again.view(torch.int32)), n
+    singles = []
     for c in range(8):
-        single = mx_gemv_gpu(wq, ws, 1.0, R, K, X[c:c + 1].contiguous())
-        for n in (2, 4, 8):
-            if c < n:
-                assert torch.equal(ys[n][c].view(torch.int32), single[0].view(torch.int32)), (c, n)
+        G.note("mx column identity %dx%d single column %d" % (R, K, c))
+        singles.append(mx_gemv_gpu(wq, ws, 1.0, R, K, X[c:c + 1].contiguous()))
+    for n in range(1, 9):
+        G.note("mx column identity %dx%d n=%d" % (R, K, n))
+        y = mx_gemv_gpu(wq, ws, 1.0, R, K, X[:n].contiguous())
+        again = mx_gemv_gpu(wq, ws, 1.0, R, K, X[:n].contiguous())
+        assert torch.equal(y.view(torch.int32), again.view(torch.int32)), n
+        for c in range(n):
+            assert torch.equal(y[c].view(torch.int32), singles[c][0].view(torch.int32)), (c, n)
 
 
 @pytest.mark.parametrize("R,K,n", [(4160, 2048, 300), (17408, 5120, 512)])

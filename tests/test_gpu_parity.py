@@ -206,23 +206,37 @@ def test_gemv_exact_special_cases():
 
 @pytest.mark.parametrize("R,K", [
     (1040, 5120),
-    # shapes whose tiles per workgroup change with the column count
+    # shapes whose tiles per workgroup change with the column count: 261
+    # tiles of 17-octet rows and 563 tiles (one tile, two past four
+    # columns), 4102 tiles (two tiles, four past four columns)
     (4176, 2064), (9000, 1040), (65620, 528),
 ])
 def test_gemv_deterministic_and_column_identity(R, K):
+    """Every width n = 1..8 gives, in column c, the bits of the one-column
+    product of X[c] (the slots, lanes and summation order of a column do not
+    depend on n), and the same bits again on a second launch.  The argmax
+    form at every width gives those logits and, per column, the row the
+    one-column argmax names."""
     wq, ws, _, _ = _prepare(R, K, 9)
     X = G.seeded_x(8, K, seed=10)
-    G.note("gemv determinism")
-    ys = {}
-    for n in (1, 2, 4, 8):
-        ys[n] = G.gemv_gpu(wq, ws, 1.0, R, K, X[:n].contiguous())
-        again = G.gemv_gpu(wq, ws, 1.0, R, K, X[:n].contiguous())
-        assert torch.equal(ys[n].view(torch.int32), again.view(torch.int32)), n
+    singles, single_am = [], []
     for c in range(8):
-        single = G.gemv_gpu(wq, ws, 1.0, R, K, X[c:c + 1].contiguous())
-        for n in (2, 4, 8):
-            if c < n:
-                assert torch.equal(ys[n][c].view(torch.int32), single[0].view(torch.int32)), (c, n)
+        G.note("column identity %dx%d single column %d" % (R, K, c))
+        singles.append(G.gemv_gpu(wq, ws, 1.0, R, K, X[c:c + 1].contiguous()))
+        lg, am = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, X[c:c + 1].contiguous())
+        assert torch.equal(lg.view(torch.int32), singles[c].view(torch.int32)), c
+        single_am.append(int(am.item()))
+    for n in range(1, 9):
+        G.note("column identity %dx%d n=%d" % (R, K, n))
+        Xn = X[:n].contiguous()
+        y = G.gemv_gpu(wq, ws, 1.0, R, K, Xn)
+        again = G.gemv_gpu(wq, ws, 1.0, R, K, Xn)
+        assert torch.equal(y.view(torch.int32), again.view(torch.int32)), n
+        logits, am = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, Xn)
+        assert torch.equal(logits.view(torch.int32), y.view(torch.int32)), n
+        for c in range(n):
+            assert torch.equal(y[c].view(torch.int32), singles[c][0].view(torch.int32)), (c, n)
+        assert [int(v) for v in am.cpu().numpy()] == single_am[:n], n
 
 
 # -------------------------------------------------------------- argmax, exact
