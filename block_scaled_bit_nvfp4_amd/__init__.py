@@ -86,11 +86,54 @@ def load():
 def _ptr(t):
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor):
-        raise TypeError("expected a torch.Tensor, got %r" % type(t))
-    if not t.is_contiguous():
-        raise ValueError("tensor must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+_BF16 = (torch.bfloat16, torch.int16)      # bf16 values or their bit patterns
+_I32 = (torch.int32,)
+_ANY = None
+
+
+def _checked(*specs):
+    """Validate the tensors of one call before any pointer reaches the
+    library: each spec is (name, tensor, allowed dtypes or None, least byte
+    count, may be None).  A tensor must be a contiguous torch.Tensor of an
+    allowed dtype holding at least the bytes the call's shape implies, and all
+    tensors must sit on one GPU (checked after the rest).  Raises TypeError or
+    ValueError; does no arithmetic on the data."""
+    device = None
+    for name, t, dtypes, nbytes, optional in specs:
+        if t is None:
+            if optional:
+                continue
+            raise ValueError("%s is required" % name)
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s: expected a torch.Tensor, got %r" % (name, type(t)))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if dtypes is not None and t.dtype not in dtypes:
+            raise ValueError("%s: dtype %s, expected %s" % (name, t.dtype, " or ".join(map(str, dtypes))))
+        have = t.numel() * t.element_size()
+        if nbytes > 0 and have < nbytes:
+            raise ValueError("%s holds %d bytes, the call needs %d" % (name, have, nbytes))
+    for name, t, _, _, _ in specs:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s must be in GPU memory (is on %s)" % (name, t.device))
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError("%s is on %s, other arguments on %s" % (name, t.device, device))
+
+
+def _prod(*v):
+    out = 1
+    for x in v:
+        out *= int(x)
+    return out
 
 
 def _stream(stream, *tensors):
@@ -123,27 +166,45 @@ def nvfp4_gemv_argmax_workspace_bytes(rows: int, cols: int, n: int) -> int:
     return int(load().nvfp4_gemv_argmax_workspace_bytes(rows, cols, n))
 
 
+def _planes(wq, ws, rows, cols, mx=False):
+    nq = (mxfp4_repacked_code_bytes if mx else nvfp4_repacked_code_bytes)(rows, cols)
+    ns = (mxfp4_repacked_scale_bytes if mx else nvfp4_repacked_scale_bytes)(rows, cols)
+    return ("wq", wq, _U8, nq, False), ("ws", ws, _U8, ns, False)
+
+
 def nvfp4_quantize(W, rows, cols, tscale, codes, scales, stream=None):
+    _checked(("W", W, _F32, 4 * _prod(rows, cols), False),
+             ("codes", codes, _U8, _prod(rows, cols) // 2, False),
+             ("scales", scales, _U8, _prod(rows, cols) // 16, False))
     _check(load().nvfp4_quantize(_ptr(W), rows, cols, float(tscale), _ptr(codes), _ptr(scales),
                                  _stream(stream, W)), "nvfp4_quantize")
 
 
 def nvfp4_repack(codes, scales, rows, cols, wq, ws, stream=None):
+    _checked(("codes", codes, _U8, _prod(rows, cols) // 2, False),
+             ("scales", scales, _U8, _prod(rows, cols) // 16, False), *_planes(wq, ws, rows, cols))
     _check(load().nvfp4_repack(_ptr(codes), _ptr(scales), rows, cols, _ptr(wq), _ptr(ws),
                                _stream(stream, codes)), "nvfp4_repack")
 
 
 def nvfp4_dequant(wq, ws, tscale, rows, cols, out_f32=None, out_bf16=None, stream=None):
+    _checked(*_planes(wq, ws, rows, cols), ("out_f32", out_f32, _F32, 4 * _prod(rows, cols), True),
+             ("out_bf16", out_bf16, _BF16, 2 * _prod(rows, cols), True))
     _check(load().nvfp4_dequant(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(out_f32),
                                 _ptr(out_bf16), _stream(stream, wq)), "nvfp4_dequant")
 
 
 def nvfp4_gemv(wq, ws, tscale, rows, cols, X, n, Y, stream=None):
+    _checked(*_planes(wq, ws, rows, cols), ("X", X, _BF16, 2 * _prod(n, cols), False),
+             ("Y", Y, _F32, 4 * _prod(n, rows), False))
     _check(load().nvfp4_gemv(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(X), int(n), _ptr(Y),
                              _stream(stream, wq)), "nvfp4_gemv")
 
 
 def nvfp4_gemv_argmax(wq, ws, tscale, rows, cols, X, n, logits, argmax, workspace, stream=None):
+    _checked(*_planes(wq, ws, rows, cols), ("X", X, _BF16, 2 * _prod(n, cols), False),
+             ("logits", logits, _F32, 4 * _prod(n, rows), True), ("argmax", argmax, _I32, 4 * int(n), False),
+             ("workspace", workspace, _ANY, 0, False))
     nbytes = workspace.numel() * workspace.element_size()
     _check(load().nvfp4_gemv_argmax(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(X), int(n),
                                     _ptr(logits), _ptr(argmax), _ptr(workspace), nbytes,
@@ -151,10 +212,13 @@ def nvfp4_gemv_argmax(wq, ws, tscale, rows, cols, X, n, logits, argmax, workspac
 
 
 def nvfp4_swiglu(gu, F, n, h, stream=None):
+    _checked(("gu", gu, _F32, 8 * _prod(n, F), False), ("h", h, _BF16, 2 * _prod(n, F), False))
     _check(load().nvfp4_swiglu(_ptr(gu), int(F), int(n), _ptr(h), _stream(stream, gu)), "nvfp4_swiglu")
 
 
 def nvfp4_gemv_swiglu(wq_gu, ws_gu, tscale, hidden, F, X, n, gu, h, stream=None):
+    _checked(*_planes(wq_gu, ws_gu, 2 * int(F), hidden), ("X", X, _BF16, 2 * _prod(n, hidden), False),
+             ("gu", gu, _F32, 8 * _prod(n, F), True), ("h", h, _BF16, 2 * _prod(n, F), False))
     _check(load().nvfp4_gemv_swiglu(_ptr(wq_gu), _ptr(ws_gu), float(tscale), int(hidden), int(F), _ptr(X),
                                     int(n), _ptr(gu), _ptr(h), _stream(stream, wq_gu)), "nvfp4_gemv_swiglu")
 
@@ -179,21 +243,30 @@ def mxfp4_repacked_scale_bytes(rows: int, cols: int) -> int:
 
 
 def mxfp4_quantize(W, rows, cols, tscale, codes, scales, stream=None):
+    _checked(("W", W, _F32, 4 * _prod(rows, cols), False),
+             ("codes", codes, _U8, _prod(rows, cols) // 2, False),
+             ("scales", scales, _U8, _prod(rows, cols) // 32, False))
     _check(load().mxfp4_quantize(_ptr(W), rows, cols, float(tscale), _ptr(codes), _ptr(scales),
                                  _stream(stream, W)), "mxfp4_quantize")
 
 
 def mxfp4_repack(codes, scales, rows, cols, wq, ws, stream=None):
+    _checked(("codes", codes, _U8, _prod(rows, cols) // 2, False),
+             ("scales", scales, _U8, _prod(rows, cols) // 32, False), *_planes(wq, ws, rows, cols, mx=True))
     _check(load().mxfp4_repack(_ptr(codes), _ptr(scales), rows, cols, _ptr(wq), _ptr(ws),
                                _stream(stream, codes)), "mxfp4_repack")
 
 
 def mxfp4_dequant(wq, ws, tscale, rows, cols, out_f32=None, out_bf16=None, stream=None):
+    _checked(*_planes(wq, ws, rows, cols, mx=True), ("out_f32", out_f32, _F32, 4 * _prod(rows, cols), True),
+             ("out_bf16", out_bf16, _BF16, 2 * _prod(rows, cols), True))
     _check(load().mxfp4_dequant(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(out_f32),
                                 _ptr(out_bf16), _stream(stream, wq)), "mxfp4_dequant")
 
 
 def mxfp4_gemv(wq, ws, tscale, rows, cols, X, n, Y, stream=None):
+    _checked(*_planes(wq, ws, rows, cols, mx=True), ("X", X, _BF16, 2 * _prod(n, cols), False),
+             ("Y", Y, _F32, 4 * _prod(n, rows), False))
     _check(load().mxfp4_gemv(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(X), int(n), _ptr(Y),
                              _stream(stream, wq)), "mxfp4_gemv")
 

@@ -201,3 +201,66 @@ def test_gemv_swiglu_validation(lib):
     assert f(A, B, 0.0, 512, 1024, C, 1, NULL, A, S0) == EINVAL
     assert f(MIS, B, 1.0, 512, 1024, C, 1, NULL, A, S0) == EALIGN
     assert f(A, B, 1.0, 512, 1024, C, 1, ctypes.c_void_p(0x100002), A, S0) == EALIGN
+
+
+# ------------------------------------------------ Python binding validation
+# The binding checks every tensor before its pointer reaches the library:
+# type, contiguity, dtype, the bytes the call's shape implies, and that all
+# of them sit on one GPU.  On this host no tensor is on a GPU, so each case
+# below is rejected by the first check it fails, which the message names.
+
+import torch  # noqa: E402
+
+
+def _t(nbytes, dtype=torch.uint8):
+    return torch.zeros(max(1, nbytes // torch.tensor([], dtype=dtype).element_size()), dtype=dtype)
+
+
+def test_binding_rejects_wrong_dtype(lib):
+    R, K = 64, 512
+    wq, ws = _t(nv.nvfp4_repacked_code_bytes(R, K)), _t(nv.nvfp4_repacked_scale_bytes(R, K))
+    X32 = torch.zeros(1, K, dtype=torch.float32)                  # fp32 activations
+    Y = torch.zeros(1, R, dtype=torch.float32)
+    with pytest.raises(ValueError, match="X: dtype"):
+        nv.nvfp4_gemv(wq, ws, 1.0, R, K, X32, 1, Y)
+    X = torch.zeros(1, K, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="Y: dtype"):
+        nv.nvfp4_gemv(wq, ws, 1.0, R, K, X, 1, Y.to(torch.float64))
+    with pytest.raises(ValueError, match="wq: dtype"):
+        nv.nvfp4_gemv(wq.to(torch.int32), ws, 1.0, R, K, X, 1, Y)
+    with pytest.raises(ValueError, match="argmax: dtype"):
+        nv.nvfp4_gemv_argmax(wq, ws, 1.0, R, K, X, 1, None, torch.zeros(1, dtype=torch.int64), _t(64))
+
+
+def test_binding_rejects_short_buffers(lib):
+    R, K = 64, 512
+    wq, ws = _t(nv.nvfp4_repacked_code_bytes(R, K)), _t(nv.nvfp4_repacked_scale_bytes(R, K))
+    X = torch.zeros(4, K, dtype=torch.bfloat16)
+    Y = torch.zeros(4, R, dtype=torch.float32)
+    with pytest.raises(ValueError, match="X holds"):
+        nv.nvfp4_gemv(wq, ws, 1.0, R, K, X[:2].contiguous(), 4, Y)   # n = 4 columns claimed, 2 given
+    with pytest.raises(ValueError, match="Y holds"):
+        nv.nvfp4_gemv(wq, ws, 1.0, R, K, X, 4, Y[:3].contiguous())
+    with pytest.raises(ValueError, match="wq holds"):
+        nv.nvfp4_gemv(wq[:-1].contiguous(), ws, 1.0, R, K, X, 4, Y)
+    with pytest.raises(ValueError, match="ws holds"):
+        nv.mxfp4_gemv(wq, _t(nv.mxfp4_repacked_scale_bytes(R, K) - 16), 1.0, R, K, X, 4, Y)
+    with pytest.raises(ValueError, match="h holds"):
+        nv.nvfp4_swiglu(torch.zeros(1, 64, dtype=torch.float32), 32, 1, torch.zeros(31, dtype=torch.int16))
+    with pytest.raises(ValueError, match="scales holds"):
+        nv.nvfp4_quantize(torch.zeros(R, K), R, K, 1.0, _t(R * K // 2), _t(R * K // 16 - 1))
+
+
+def test_binding_rejects_host_and_strided_tensors(lib):
+    R, K = 64, 512
+    wq, ws = _t(nv.nvfp4_repacked_code_bytes(R, K)), _t(nv.nvfp4_repacked_scale_bytes(R, K))
+    X = torch.zeros(1, K, dtype=torch.bfloat16)
+    Y = torch.zeros(1, R, dtype=torch.float32)
+    with pytest.raises(ValueError, match="must be in GPU memory"):
+        nv.nvfp4_gemv(wq, ws, 1.0, R, K, X, 1, Y)
+    with pytest.raises(ValueError, match="contiguous"):
+        nv.nvfp4_gemv(wq, ws, 1.0, R, K, torch.zeros(K, 2, dtype=torch.bfloat16).t(), 1, Y)
+    with pytest.raises(TypeError):
+        nv.nvfp4_gemv(wq, ws, 1.0, R, K, [0] * K, 1, Y)
+    with pytest.raises(ValueError, match="is required"):
+        nv.nvfp4_gemv(wq, ws, 1.0, R, K, X, 1, None)
