@@ -232,7 +232,8 @@ int launch_narrow_tww(const Geometry &g, const NarrowConfig &cfg, const uint8_t 
                       float tscale, const uint16_t *X, int n, float *Y, unsigned long long *amax_ws,
                       int up_st, uint16_t *h, int waves, int64_t groups, hipStream_t stream) {
     const dim3 grid{unsigned(groups)}, block{unsigned(kLanes * waves)};
-    const size_t lds = size_t(waves) * (size_t(narrow_wave_lds_bytes(n)) + size_t(n) * TWW * kTileRows * sizeof(float));
+    const size_t lds = narrow_lds_bytes(waves, n, TWW);
+    if (lds > kNarrowLdsLimit) return NVFP4_EINVAL;
     const int rows = int(g.rows), octets = int(g.octets), kb = int(g.kb), K = int(g.cols);
 #define NVFP4_LAUNCH(NN)                                                                                      \
     hipLaunchKernelGGL((narrow_kernel<NN, TWW, MODE, FMT>), grid, block, lds, stream, wq, ws, tscale, rows, octets, \
@@ -301,7 +302,14 @@ int launch_gemv_swiglu(const uint8_t *wq, const uint8_t *ws, float tscale, int64
                            F * n, h);
         return launch_status();
     }
-    const NarrowConfig cfg = narrow_config(g, n);
+    NarrowConfig cfg = narrow_config(g, n);
+    // A workgroup holds both halves' waves; where their LDS would pass the
+    // limit (four tiles at 16 waves past four columns) it takes fewer tiles,
+    // which changes no row's summation order.
+    while (cfg.tww > 1 && narrow_lds_bytes(2 * cfg.ksplit, n, cfg.tww) > kNarrowLdsLimit) {
+        cfg.tww /= 2;
+        cfg.groups = g.supertiles * (kSuperTiles / cfg.tww);
+    }
     const int64_t groups = cfg.groups / 2;   // the gate half's workgroups
     const int up_st = int(F / kSuperRows);
     switch (cfg.tww) {

@@ -45,6 +45,7 @@
 // workgroups of one XCD (workgroup b runs on XCD b mod 8), so a row group's
 // weights are fetched from HBM into that XCD's L2 once and re-read there by
 // the other column tiles.
+#include <mutex>
 #include <type_traits>
 
 #include "nvfp4_host.h"
@@ -462,20 +463,40 @@ wide_kernel_mxfp4(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws
     wide_body<kMxfp4>(wq, ws, tscale, rows, supertiles, octets, K, X, n, Y, row_groups, col_groups, extra, vec_store);
 }
 
+// Per-device facts the wide launch needs, taken once per device on its first
+// wide call (with that device current): the CU count, which the
+// decomposition follows, and the dynamic-LDS attribute of both wide kernels,
+// whose rings (148 KiB) are above the default limit.  Later calls only look
+// up the current device's index.
+constexpr int kMaxDevices = 64;
+struct WideDevice {
+    std::once_flag once;
+    int cus = 0;
+    bool lds_ok = false;
+};
+static WideDevice g_wide_devices[kMaxDevices];
+
+static const WideDevice *wide_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    WideDevice &w = g_wide_devices[dev];
+    std::call_once(w.once, [&w, dev] {
+        if (hipDeviceGetAttribute(&w.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) w.cus = 0;
+        w.lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(wide_kernel_nvfp4),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds) == hipSuccess &&
+                   hipFuncSetAttribute(reinterpret_cast<const void *>(wide_kernel_mxfp4),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds) == hipSuccess;
+    });
+    return &w;
+}
+
 int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
                 int n, float *Y, hipStream_t stream, int fmt) {
     if (g.cols > kMaxWideCols || int64_t(g.scale_bytes(fmt)) > kMaxWideScaleBytes) return NVFP4_ESHAPE;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 0;
-    const WideConfig c = wide_config(g, n, cus);
+    const WideDevice *wd = wide_device();
+    if (!wd || !wd->lds_ok) return NVFP4_EHIP;
+    const WideConfig c = wide_config(g, n, wd->cus);
     if (c.groups > (int64_t(1) << 31) - 1) return NVFP4_ESHAPE;
-    // The rings (148 KiB) are above the default dynamic-LDS limit.
-    const void *kern = fmt == kMxfp4 ? reinterpret_cast<const void *>(wide_kernel_mxfp4)
-                                     : reinterpret_cast<const void *>(wide_kernel_nvfp4);
-    if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds) != hipSuccess)
-        return NVFP4_EHIP;
     const int vec = int(aligned(Y, 16) && g.rows % 4 == 0);
     if (fmt == kMxfp4)
         hipLaunchKernelGGL(wide_kernel_mxfp4, dim3(unsigned(c.groups)), dim3(kWideWaves * kLanes), kWideLds,

@@ -111,6 +111,14 @@ inline NarrowConfig narrow_config(const Geometry &g, int n, int max_tww = 4) {
 // one slot of compact activations (1 KiB per four columns).
 constexpr int narrow_wave_lds_bytes(int n) { return 256 + (n > 4 ? 2 : 1) * 1024; }
 
+// Dynamic LDS of a narrow workgroup: each wave's slot, then the partial sums
+// of its tiles' rows for every column.  Kept within the default 64 KiB
+// dynamic limit, so no launch needs a function attribute.
+constexpr size_t narrow_lds_bytes(int waves, int n, int tww) {
+    return size_t(waves) * (size_t(narrow_wave_lds_bytes(n)) + size_t(n) * tww * kTileRows * sizeof(float));
+}
+constexpr size_t kNarrowLdsLimit = 65536;
+
 // Argmax key: order-preserving map of an fp32 value (with -0 folded into +0)
 // in the high word, the complement of the row index in the low word, so the
 // unsigned maximum picks the largest value and, among equals, the lowest row.

@@ -43,7 +43,10 @@ NOT_FUSED = {(4096, 1024), (8192, 1024)}
                                    (1008, 1024, 5),
                                    # past four columns: two tiles per workgroup
                                    # (520 stacked tiles), four (4104 tiles)
-                                   (1040, 4160, 6), (512, 32832, 5)])
+                                   (1040, 4160, 6), (512, 32832, 5),
+                                   # four tiles would pass the 64 KiB LDS of a
+                                   # 16-wave workgroup: it takes two
+                                   (1024, 32832, 8)])
 def test_gemv_swiglu_equals_two_launches(D, F, n):
     import block_scaled_bit_nvfp4_amd as nv
     _, q, ss = _stacked(D, F, seed=D + F)
