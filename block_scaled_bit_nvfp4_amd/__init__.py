@@ -19,7 +19,7 @@ __all__ = [
     "NVFP4Error", "library_path", "load",
     "nvfp4_strerror", "nvfp4_repacked_code_bytes", "nvfp4_repacked_scale_bytes",
     "nvfp4_quantize", "nvfp4_repack", "nvfp4_dequant", "nvfp4_gemv",
-    "nvfp4_gemv_argmax_workspace_bytes", "nvfp4_gemv_argmax", "nvfp4_swiglu",
+    "nvfp4_gemv_argmax_workspace_bytes", "nvfp4_gemv_argmax", "nvfp4_gemv_argmax_noalloc", "nvfp4_swiglu",
     "nvfp4_gemv_swiglu",
     "mxfp4_repacked_code_bytes", "mxfp4_repacked_scale_bytes", "mxfp4_quantize", "mxfp4_repack",
     "mxfp4_dequant", "mxfp4_gemv",
@@ -66,6 +66,7 @@ def load():
             "nvfp4_gemv": (i32, [P, P, f32, i64, i64, P, i32, P, P]),
             "nvfp4_gemv_argmax_workspace_bytes": (sz, [i64, i64, i32]),
             "nvfp4_gemv_argmax": (i32, [P, P, f32, i64, i64, P, i32, P, P, P, sz, P]),
+            "nvfp4_gemv_argmax_noalloc": (i32, [P, P, f32, i64, i64, P, i32, P, P, P]),
             "nvfp4_swiglu": (i32, [P, i64, i32, P, P]),
             "nvfp4_gemv_swiglu": (i32, [P, P, f32, i64, i64, P, i32, P, P, P]),
             "mxfp4_repacked_code_bytes": (sz, [i64, i64]),
@@ -209,6 +210,14 @@ def nvfp4_gemv_argmax(wq, ws, tscale, rows, cols, X, n, logits, argmax, workspac
     _check(load().nvfp4_gemv_argmax(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(X), int(n),
                                     _ptr(logits), _ptr(argmax), _ptr(workspace), nbytes,
                                     _stream(stream, wq)), "nvfp4_gemv_argmax")
+
+
+def nvfp4_gemv_argmax_noalloc(wq, ws, tscale, rows, cols, X, n, logits, argmax, stream=None):
+    _checked(*_planes(wq, ws, rows, cols), ("X", X, _BF16, 2 * _prod(n, cols), False),
+             ("logits", logits, _F32, 4 * _prod(n, rows), True), ("argmax", argmax, _I32, 4 * int(n), False))
+    _check(load().nvfp4_gemv_argmax_noalloc(_ptr(wq), _ptr(ws), float(tscale), rows, cols, _ptr(X), int(n),
+                                            _ptr(logits), _ptr(argmax), _stream(stream, wq)),
+           "nvfp4_gemv_argmax_noalloc")
 
 
 def nvfp4_swiglu(gu, F, n, h, stream=None):

@@ -14,6 +14,8 @@
 // that take contiguous octet ranges of the rows (nvfp4_narrow.h); the waves'
 // partial sums meet in LDS and are added in wave order.  Everything depends
 // only on (rows, cols), never on n or on timing.
+#include <mutex>
+
 #include "nvfp4_narrow.h"
 
 namespace nvfp4 {
@@ -354,17 +356,12 @@ NVFP4_API size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, i
     return size_t(narrow_config(Geometry(rows, cols), n).groups) * size_t(n) * sizeof(unsigned long long);
 }
 
-NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
-                                int64_t cols, const uint16_t *X, int n, float *logits, int32_t *argmax,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!argmax || !workspace) return NVFP4_EINVAL;
-    if (int st = check_product_args(wq, ws, tscale, rows, cols, X, n)) return st;
-    if (n > kMaxNarrowN) return NVFP4_EINVAL;
-    if (!aligned(logits, 4) || !aligned(argmax, 4) || !aligned(workspace, 8)) return NVFP4_EALIGN;
-    if (workspace_bytes < nvfp4_gemv_argmax_workspace_bytes(rows, cols, n)) return NVFP4_EWORKSPACE;
-    const Geometry g(rows, cols);
+// The argmax's two launches with `keys` as the product's workspace; the
+// arguments are already validated.
+static int launch_gemv_argmax(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale,
+                              const uint16_t *X, int n, float *logits, int32_t *argmax, unsigned long long *keys,
+                              hipStream_t stream) {
     (void)hipGetLastError();
-    auto *keys = static_cast<unsigned long long *>(workspace);
     if (int st = launch_narrow<kArgmax>(g, wq, ws, tscale, X, n, logits, keys, stream)) return st;
     const int groups = int(narrow_config(g, n).groups);
 #define NVFP4_FINISH(NN) \
@@ -381,6 +378,66 @@ NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tsca
     }
 #undef NVFP4_FINISH
     return launch_status();
+}
+
+static int check_argmax_args(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
+                             const uint16_t *X, int n, float *logits, int32_t *argmax) {
+    if (!argmax) return NVFP4_EINVAL;
+    if (int st = check_product_args(wq, ws, tscale, rows, cols, X, n)) return st;
+    if (n > kMaxNarrowN) return NVFP4_EINVAL;
+    if (!aligned(logits, 4) || !aligned(argmax, 4)) return NVFP4_EALIGN;
+    return NVFP4_OK;
+}
+
+NVFP4_API int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
+                                int64_t cols, const uint16_t *X, int n, float *logits, int32_t *argmax,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!workspace) return NVFP4_EINVAL;
+    if (int st = check_argmax_args(wq, ws, tscale, rows, cols, X, n, logits, argmax)) return st;
+    if (!aligned(workspace, 8)) return NVFP4_EALIGN;
+    if (workspace_bytes < nvfp4_gemv_argmax_workspace_bytes(rows, cols, n)) return NVFP4_EWORKSPACE;
+    return launch_gemv_argmax(Geometry(rows, cols), wq, ws, tscale, X, n, logits, argmax,
+                              static_cast<unsigned long long *>(workspace), stream);
+}
+
+// ------------------------------------------- the argmax without a workspace
+
+// The key workspace of nvfp4_gemv_argmax_noalloc: one static array per GPU,
+// loaded with the library's code object and held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address); it passes the address that
+// hipGetSymbolAddress gives on that device, looked up once per device on the
+// entry point's first call there, with that device current.
+static __device__ __align__(256) unsigned long long scratch[NVFP4_ARGMAX_SCRATCH_BYTES / sizeof(unsigned long long)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+struct ScratchDevice {
+    std::once_flag once;
+    unsigned long long *ptr = nullptr;
+};
+ScratchDevice g_scratch[kMaxScratchDevices];
+
+unsigned long long *scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    ScratchDevice &d = g_scratch[dev];
+    std::call_once(d.once, [&d] {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) d.ptr = static_cast<unsigned long long *>(p);
+    });
+    return d.ptr;
+}
+}  // namespace
+
+NVFP4_API int nvfp4_gemv_argmax_noalloc(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
+                                        int64_t cols, const uint16_t *X, int n, float *logits, int32_t *argmax,
+                                        hipStream_t stream) {
+    if (int st = check_argmax_args(wq, ws, tscale, rows, cols, X, n, logits, argmax)) return st;
+    if (nvfp4_gemv_argmax_workspace_bytes(rows, cols, n) > NVFP4_ARGMAX_SCRATCH_BYTES) return NVFP4_EWORKSPACE;
+    unsigned long long *keys = scratch_on_current_device();
+    if (!keys) return NVFP4_EHIP;
+    return launch_gemv_argmax(Geometry(rows, cols), wq, ws, tscale, X, n, logits, argmax, keys, stream);
 }
 
 NVFP4_API int nvfp4_gemv_swiglu(const uint8_t *wq_gu, const uint8_t *ws_gu, float tscale, int64_t hidden,

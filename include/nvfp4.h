@@ -166,6 +166,26 @@ int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_
                       int64_t cols, const uint16_t *X, int n, float *logits, int32_t *argmax,
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Largest workspace nvfp4_gemv_argmax_noalloc serves: 1 MiB, enough for
+ * every n <= 8 up to 262144 rows (4 bytes per row bound the workspace). */
+#define NVFP4_ARGMAX_SCRATCH_BYTES (1u << 20)
+
+/* nvfp4_gemv_argmax without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The keys
+ * go to a static device array of NVFP4_ARGMAX_SCRATCH_BYTES that the library
+ * holds on each GPU until the process ends (its address is looked up once per
+ * device, on the first call there).  Same kernels, same results, bit for
+ * bit, as nvfp4_gemv_argmax.  NVFP4_EWORKSPACE when
+ * nvfp4_gemv_argmax_workspace_bytes(rows, cols, n) exceeds that size;
+ * NVFP4_EHIP if the array's address cannot be found.  Every call on one GPU
+ * shares its array: calls that may overlap on one GPU (several streams, or
+ * several host threads) race and must be serialised by the caller.  The
+ * array needs no clearing: each call writes every key it reads. */
+int nvfp4_gemv_argmax_noalloc(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
+                              int64_t cols, const uint16_t *X, int n, float *logits, int32_t *argmax,
+                              hipStream_t stream);
+
 /* SwiGLU between the MLP matvecs: gu fp32 [n][2F] holds the stacked gate
  * (columns 0..F-1) and up (F..2F-1) outputs; h [n][F] bf16 bits =
  * bf16_nearest_even(g * u / (1 + exp(-g))) computed in fp32 (the pages'

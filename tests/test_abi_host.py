@@ -264,3 +264,14 @@ def test_binding_rejects_host_and_strided_tensors(lib):
         nv.nvfp4_gemv(wq, ws, 1.0, R, K, [0] * K, 1, Y)
     with pytest.raises(ValueError, match="is required"):
         nv.nvfp4_gemv(wq, ws, 1.0, R, K, X, 1, None)
+
+
+def test_argmax_noalloc_validation(lib):
+    g = lib.nvfp4_gemv_argmax_noalloc
+    # the keys of 2^20 rows at n = 8 fill the 1 MiB array; one row more is
+    # rejected before any HIP call
+    assert g(A, B, 1.0, (1 << 20) + 1, 16, C, 8, NULL, A, S0) == EWORKSPACE
+    assert g(A, B, 1.0, 16, 32, C, 9, NULL, A, S0) == EINVAL      # argmax is n <= 8
+    assert g(A, B, 1.0, 16, 32, C, 4, NULL, NULL, S0) == EINVAL
+    assert g(A, B, 1.0, 16, 32, C, 4, ctypes.c_void_p(0x300002), A, S0) == EALIGN
+    assert g(MIS, B, 1.0, 16, 32, C, 4, NULL, A, S0) == EALIGN
