@@ -16,6 +16,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libnvfp4.so")
+# The measurement aid bench.py times the products against (nvfp4_probe.h).
+PROBE_SRC = os.path.join(PKG, "probe", "nvfp4_probe.hip")
+PROBE_LIB_PATH = os.path.join(PKG, "libnvfp4_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -48,22 +51,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every .hip source for gfx950 and link libnvfp4.so (always rebuilds)."""
-    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
-        raise RuntimeError("hipcc not found (%s)" % HIPCC)
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every .hip source for gfx950 and link libnvfp4.so, and the
+    measurement probe into libnvfp4_probe.so (always rebuilds)."""
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        raise RuntimeError("hipcc not found (%s)" % HIPCC)
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources() + [PROBE_SRC]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:-1], LIB_PATH)
+    _link(objs[-1:], PROBE_LIB_PATH)
     if verbose:
-        print("built", LIB_PATH)
+        print("built", LIB_PATH, "and", PROBE_LIB_PATH)
     return LIB_PATH
 
 

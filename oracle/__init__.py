@@ -64,6 +64,8 @@ def _load():
         i64 = ctypes.c_int64
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.restype = None
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         lib.oracle_e2m1_value.restype = ctypes.c_double
         lib.oracle_e2m1_value.argtypes = [ctypes.c_int]
         lib.oracle_e4m3_value.restype = ctypes.c_double
@@ -117,6 +119,12 @@ def _check_shape(R: int, K: int):
 def num_threads() -> int:
     """Threads the oracle's row-parallel loops use (OpenMP)."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's row-parallel loops (timing; results do not
+    depend on it: every output is one sequential k-sum)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def e2m1_value(code: int) -> float:

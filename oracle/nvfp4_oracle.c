@@ -52,6 +52,17 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Sets the threads of the row-parallel loops (timing only: every output is
+ * one sequential k-sum, so results do not depend on the count). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---------------------------------------------------------------- decode -- */
 
 /* E2M1 code (4 bits) -> exact value.  Bit 3 sign, bits 2..1 exponent (bias 1),
