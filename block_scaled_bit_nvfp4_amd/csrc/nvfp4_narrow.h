@@ -28,9 +28,9 @@
 // row's octets (8 blocks) over `ksplit` waves; each wave streams its octets
 // with range-checked buffer loads, one octet ahead of the MFMAs: per tile one
 // 16-byte code load (the tile's 1 KiB chunk), the scales of its rows, and one
-// compact 16-byte activation load per four columns (for one column and
-// several tiles the activations and scales of four octets come in one load
-// each, a group ahead).  Loads past the wave's last octet read zeros with no
+// compact 16-byte activation load per four columns (for one column the
+// activations and scales of four octets come in one load each, a group
+// ahead).  Loads past the wave's last octet read zeros with no
 // memory traffic, so the loop needs no branch around a load.
 //
 // A operands: the wave writes the octet's compact activations to its own LDS
@@ -276,13 +276,14 @@ __device__ __forceinline__ void narrow_accumulate(const uint8_t *__restrict__ wq
         }
     };
 
-    if constexpr (N == 1 && TWW >= 2) {
-        // One column, several tiles: the activations and scales of four
-        // octets come in one load each (per scale load 4 / TWW octets), a
-        // group ahead of use, so an octet costs the wave its code loads alone.
-        // Vector-memory instructions, more than bytes, are what the small
-        // per-octet activation and scale loads cost (the 5120 x 17408 down
-        // product 6 % faster; one-tile workgroups measured no better).  Lane 16j + 4p + q holds
+    if constexpr (N == 1) {
+        // One column: the activations and scales of four octets come in one
+        // load each (per scale load 4 / TWW octets), a group ahead of use, so
+        // an octet costs the wave its code loads alone.  Vector-memory
+        // instructions, more than bytes, are what the small per-octet
+        // activation and scale loads cost (the 5120 x 17408 down product 6 %
+        // faster, 17408 x 5120 5 %, the 8192 x 4096 draft head 4 %; the same
+        // bits as per-octet loads).  Lane 16j + 4p + q holds
         // X[128(ob + j) + 32p + 8q ..]; the group's 1 KiB goes to the slot,
         // where octet j's A operands are read at 256 j.  Scale load i: lane
         // 16 (TWW a + t) + r holds row r of tile t for octet ob + OPS i + a.
