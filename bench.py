@@ -8,7 +8,8 @@ process:
     C1 gemv_256x512         single 256x512 matvec, N=1 (latency-bound; parity case)
     C2 decode_4096x4096     decode GEMV, 64 distinct 4096x4096 matrices rotated, N=1
     C3 mlp_27b_decode       gate||up 34816x5120 + SwiGLU, down 5120x17408, 8 layers rotated, N=1
-    C4 verify_vocab_n4      17408x5120 and a 151936x5120 vocabulary head with argmax, N=4
+    C4 verify_vocab_n4      17408x5120 and a 151936x5120 vocabulary head with argmax in one
+                            launch (nvfp4_gemv_batch), N=4
     C5 prefill_n512         17408x5120 at N=512 on MFMA, 4 layer copies rotated
 
 A step is one pass over a configuration's whole weight set, replayed as one
@@ -157,13 +158,19 @@ class Step:
             self.y1 = torch.empty(n, mw.rows, dtype=torch.float32, device=DEV)
             self.logits = torch.empty(n, head.rows, dtype=torch.float32, device=DEV)
             self.am = torch.empty(n, dtype=torch.int32, device=DEV)
-            self.wsp = torch.empty(nv.nvfp4_gemv_argmax_workspace_bytes(head.rows, head.cols, n), dtype=torch.uint8,
-                                   device=DEV)
-            self.launches.append(Launch(self._gemv(self.M1, self.x, n, self.y1), gemv_bytes(mw.rows, mw.cols, n),
-                                        2 * n * mw.rows * mw.cols, "matvec %dx%d" % (mw.rows, mw.cols), ("w", 0)))
-            self.launches.append(Launch(self._argmax(self.M2, self.logits, self.am),
-                                        gemv_bytes(head.rows, head.cols, n) + 4 * n, 2 * n * head.rows * head.cols,
-                                        "matvec+argmax %dx%d" % (head.rows, head.cols), ("lm_head", 0)))
+            # both products in one launch of the matvec, then the head's
+            # argmax finish (nvfp4_gemv_batch)
+            self.prods = [dict(wq=self.M2.wq, ws=self.M2.ws, tscale=self.M2.tscale, rows=head.rows, y=self.logits,
+                               argmax=self.am),
+                          dict(wq=self.M1.wq, ws=self.M1.ws, tscale=self.M1.tscale, rows=mw.rows, y=self.y1)]
+            self.wsp = torch.empty(max(8, nv.nvfp4_gemv_batch_workspace_bytes(self.prods, mw.cols, n)),
+                                   dtype=torch.uint8, device=DEV)
+            self.launches.append(Launch(self._verify_batch(mw.cols),
+                                        gemv_bytes(mw.rows, mw.cols, n) + gemv_bytes(head.rows, head.cols, n)
+                                        - n * mw.cols * 2 + 4 * n,
+                                        2 * n * (mw.rows + head.rows) * mw.cols,
+                                        "matvec+argmax batch %dx%d, %dx%d" % (head.rows, head.cols, mw.rows, mw.cols),
+                                        ("w+lm_head", 0)))
         elif name == "draft_head_8192x4096":
             m = w.matrices[0]
             self.x = wl.activations(1, m.cols, seed=wl.seed_of(name, "x"), device=DEV)
@@ -214,6 +221,11 @@ class Step:
             nv.nvfp4_gemv_argmax(M.wq, M.ws, M.tscale, M.rows, M.cols, self.x, self.n, logits, am, self.wsp)
         return f
 
+    def _verify_batch(self, cols):
+        def f():
+            nv.nvfp4_gemv_batch(self.prods, cols, self.x, self.n, self.wsp)
+        return f
+
     def run(self, kernels=None):
         for L in self.launches:
             if kernels is None or L.kernel in kernels:
@@ -260,10 +272,11 @@ def time_graph(run, steps, warmup, per_graph=1):
 # Steps per graph replay.  A replay costs about 10 us of launch before its
 # first kernel (the 256 x 512 case measures it), which a whole-model decode
 # graph pays once per token over hundreds of launches.  Steps of only a few
-# launches therefore go several to a replay, where that adds no cache reuse:
-# the 256 x 512 case is cache-resident anyway, and every verify step streams
-# the 440 MB vocabulary head, which evicts the previous step's bytes from the
-# 256 MB Infinity Cache.  The other workloads have 4 to 64 launches per step.
+# launches therefore go several to a replay, which charges that cost to all
+# of them; this repeats no cached work: the 256 x 512 case is
+# cache-resident anyway, and every verify step streams the 440 MB
+# vocabulary head, which evicts the previous step's bytes from the 256 MB
+# Infinity Cache.  The other workloads have 4 to 64 launches per step.
 STEP_BATCH = {"gemv_256x512": 16, "verify_vocab_n4": 4, "verify_vocab_n8": 4}
 INFINITY_CACHE = 256 << 20
 
@@ -403,19 +416,22 @@ def cpu_baseline(step, budget_s=12.0, min_s=8.0):
     sample = []
     if w.name in ("gemv_256x512", "decode_4096x4096", "mxfp4_gemv_17408x5120", "draft_head_8192x4096"):
         for M in step.mats:
-            sample.append((M, step.x, None))
+            sample.append((M, step.x, None, None))
     elif w.name == "mlp_27b_decode":
         for G_, D in step.layers:
-            sample.append((G_, step.x, None))
+            sample.append((G_, step.x, None, None))
     elif w.name in ("verify_vocab_n4", "verify_vocab_n8"):
-        sample.append((step.M1, step.x, None))
-        sample.append((step.M2, step.x, np.arange(0, step.M2.rows, 8)))
+        # the step's own outputs (both products of its one batched launch)
+        step.run()
+        torch.cuda.synchronize()
+        sample.append((step.M1, step.x, None, step.y1.cpu().numpy()))
+        sample.append((step.M2, step.x, np.arange(0, step.M2.rows, 8), step.logits.cpu().numpy()))
     elif w.name in MFMA_WORKLOADS:
-        sample.append((step.M, step.x, np.arange(0, step.M.rows, 256)))
+        sample.append((step.M, step.x, np.arange(0, step.M.rows, 256), None))
     gemv = oracle.mx_gemv if w.fmt == "mxfp4" else oracle.gemv
     xb_cache, prepared = {}, []
     t_total, bytes_done, flops_done, checked, worst, outputs = 0.0, 0, 0, 0, 0.0, 0
-    for M, x, rows in sample:
+    for M, x, rows, out in sample:
         if t_total >= budget_s:
             break
         Wf = wl.weights(M.rows, M.cols, seed=wl.seed_of(w.name, M.name, M.copy), outliers=w.outliers, device=DEV)
@@ -437,9 +453,11 @@ def cpu_baseline(step, budget_s=12.0, min_s=8.0):
         bytes_done += nbytes
         flops_done += 2 * n * len(rsel) * M.cols
         outputs += Y_ref.size
-        y = torch.empty(n, M.rows, dtype=torch.float32, device=DEV)
-        M.gemv(x, n, y)
-        yg = y.cpu().numpy()[:, rsel].astype(np.float64)
+        if out is None:
+            y = torch.empty(n, M.rows, dtype=torch.float32, device=DEV)
+            M.gemv(x, n, y)
+            out = y.cpu().numpy()
+        yg = out[:, rsel].astype(np.float64)
         err = np.abs(yg - Y_ref) / (1e-5 * S + 1e-6)
         worst = max(worst, float(err.max()))
         checked += err.size

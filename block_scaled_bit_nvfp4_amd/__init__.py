@@ -20,7 +20,7 @@ __all__ = [
     "nvfp4_strerror", "nvfp4_repacked_code_bytes", "nvfp4_repacked_scale_bytes",
     "nvfp4_quantize", "nvfp4_repack", "nvfp4_dequant", "nvfp4_gemv",
     "nvfp4_gemv_argmax_workspace_bytes", "nvfp4_gemv_argmax", "nvfp4_gemv_argmax_noalloc", "nvfp4_swiglu",
-    "nvfp4_gemv_swiglu",
+    "nvfp4_gemv_swiglu", "nvfp4_gemv_batch", "nvfp4_gemv_batch_workspace_bytes", "NVFP4_MAX_BATCH",
     "mxfp4_repacked_code_bytes", "mxfp4_repacked_scale_bytes", "mxfp4_quantize", "mxfp4_repack",
     "mxfp4_dequant", "mxfp4_gemv",
     "alloc_repacked", "alloc_mx_repacked",
@@ -32,6 +32,13 @@ _lock = threading.Lock()
 _lib = None
 
 NVFP4_MAX_N = 65536
+NVFP4_MAX_BATCH = 4
+
+
+class _Product(ctypes.Structure):
+    """struct nvfp4_product of nvfp4.h."""
+    _fields_ = [("wq", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("tscale", ctypes.c_float),
+                ("rows", ctypes.c_int64), ("y", ctypes.c_void_p), ("argmax", ctypes.c_void_p)]
 
 
 class NVFP4Error(RuntimeError):
@@ -69,6 +76,8 @@ def load():
             "nvfp4_gemv_argmax_noalloc": (i32, [P, P, f32, i64, i64, P, i32, P, P, P]),
             "nvfp4_swiglu": (i32, [P, i64, i32, P, P]),
             "nvfp4_gemv_swiglu": (i32, [P, P, f32, i64, i64, P, i32, P, P, P]),
+            "nvfp4_gemv_batch_workspace_bytes": (sz, [P, i32, i64, i32]),
+            "nvfp4_gemv_batch": (i32, [P, i32, i64, P, i32, P, sz, P]),
             "mxfp4_repacked_code_bytes": (sz, [i64, i64]),
             "mxfp4_repacked_scale_bytes": (sz, [i64, i64]),
             "mxfp4_quantize": (i32, [P, i64, i64, f32, P, P, P]),
@@ -230,6 +239,43 @@ def nvfp4_gemv_swiglu(wq_gu, ws_gu, tscale, hidden, F, X, n, gu, h, stream=None)
              ("gu", gu, _F32, 8 * _prod(n, F), True), ("h", h, _BF16, 2 * _prod(n, F), False))
     _check(load().nvfp4_gemv_swiglu(_ptr(wq_gu), _ptr(ws_gu), float(tscale), int(hidden), int(F), _ptr(X),
                                     int(n), _ptr(gu), _ptr(h), _stream(stream, wq_gu)), "nvfp4_gemv_swiglu")
+
+
+def _batch(products, cols, n, X=None, workspace=None):
+    """Product descriptions (dicts with wq, ws, tscale, rows and optional y,
+    argmax) -> (ctypes array of nvfp4_product, count), after the same tensor
+    checks as the single-product calls."""
+    products = list(products)
+    specs = []
+    for i, q in enumerate(products):
+        rows = int(q["rows"])
+        wq, ws = _planes(q["wq"], q["ws"], rows, cols)
+        specs += [("products[%d].wq" % i,) + wq[1:], ("products[%d].ws" % i,) + ws[1:],
+                  ("products[%d].y" % i, q.get("y"), _F32, 4 * _prod(n, rows), True),
+                  ("products[%d].argmax" % i, q.get("argmax"), _I32, 4 * int(n), True)]
+    if X is not None:
+        specs.append(("X", X, _BF16, 2 * _prod(n, cols), False))
+    specs.append(("workspace", workspace, _ANY, 0, True))
+    _checked(*specs)
+    arr = (_Product * max(1, len(products)))()
+    for i, q in enumerate(products):
+        arr[i] = _Product(_ptr(q["wq"]), _ptr(q["ws"]), float(q["tscale"]), int(q["rows"]), _ptr(q.get("y")),
+                          _ptr(q.get("argmax")))
+    return arr, len(products)
+
+
+def nvfp4_gemv_batch_workspace_bytes(products, cols, n) -> int:
+    arr, count = _batch(products, cols, n)
+    return int(load().nvfp4_gemv_batch_workspace_bytes(arr, count, int(cols), int(n)))
+
+
+def nvfp4_gemv_batch(products, cols, X, n, workspace=None, stream=None):
+    """Several products of one X in one launch (nvfp4_gemv_batch); products:
+    dicts with wq, ws, tscale, rows, and y and/or argmax tensors."""
+    arr, count = _batch(products, cols, n, X, workspace)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().nvfp4_gemv_batch(arr, count, int(cols), _ptr(X), int(n), _ptr(workspace), nbytes,
+                                   _stream(stream, X)), "nvfp4_gemv_batch")
 
 
 def alloc_repacked(rows: int, cols: int, device="cuda"):

@@ -43,6 +43,57 @@ __global__ void __launch_bounds__(256) swiglu_kernel(const float *__restrict__ g
 
 // ------------------------------------------------------------ the products
 
+// The epilogue of the narrow products.  LDS: each wave's slot
+// (narrow_wave_lds_bytes), then the waves' partial sums
+// red[(wave * N + c) * SEG + row of the workgroup], SEG = TWW * 16 rows.
+template <int N, int TWW>
+__device__ __forceinline__ void store_partials(float *red, int wave, int lane, const float (&acc)[TWW][N > 4 ? 2 : 1]) {
+    constexpr int SEG = TWW * kTileRows;
+    const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int tt = 0; tt < TWW; ++tt)
+#pragma unroll
+        for (int hh = 0; hh < (N > 4 ? 2 : 1); ++hh) {
+            const int c = g + 4 * hh;
+            if (c < N) red[(wave * N + c) * SEG + tt * kTileRows + r] = acc[tt][hh];
+        }
+}
+
+// After the barrier: the waves' partials of each (column, row) added in wave
+// order, times tscale, stored to Y [N][rows] (when Y is not NULL); with keys
+// not NULL, the workgroup's largest argmax key of each column goes to
+// keys[c].  row0 is the workgroup's first row.
+template <int N, int TWW>
+__device__ __forceinline__ void finish_rows(const float *red, int ksplit, float tscale, int rows, int row0,
+                                            float *__restrict__ Y, unsigned long long *__restrict__ keys) {
+    constexpr int SEG = TWW * kTileRows;
+    // Segments of SEG consecutive threads hold one column's rows; blockDim is
+    // a multiple of 64 and SEG divides 64, so a segment never straddles a
+    // wave or an iteration.
+    for (int idx = threadIdx.x; idx < N * SEG; idx += blockDim.x) {
+        // every wave's partial is read before the first add (clamped indices,
+        // adds in wave order): one LDS round trip instead of one per batch
+        const int c = idx / SEG, lr = idx % SEG;
+        float part[kMaxKsplit];
+#pragma unroll
+        for (int w = 0; w < kMaxKsplit; ++w) part[w] = red[((w < ksplit ? w : 0) * N + c) * SEG + lr];
+        float tot = part[0];
+#pragma unroll
+        for (int w = 1; w < kMaxKsplit; ++w)
+            if (w < ksplit) tot += part[w];
+        const float y = tot * tscale;
+        const int row = row0 + lr;
+        const bool valid = row < rows;
+        if (valid && Y) Y[int64_t(c) * rows + row] = y;
+        if (keys) {
+            // the segment's SEG lanes are all active (SEG divides 64; keys is
+            // the same for the whole workgroup)
+            const unsigned long long key = lanes_max_u64<SEG>(valid ? argmax_key(y, uint32_t(row)) : 0ull);
+            if (lr == 0) keys[c] = key;
+        }
+    }
+}
+
 // MODE kPlain:  Y[c][row] = tscale * sum.
 // MODE kArgmax: as kPlain (Y may be NULL) plus, per column, the largest
 //   argmax key of the workgroup's rows stored to amax_ws[blockIdx][c];
@@ -76,16 +127,7 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
     float acc[TWW][H];
     narrow_accumulate<N, TWW, FMT>(wq, ws, int64_t(st) + (half ? up_st : 0), tg, o0, o1, octets, kb, X, K, lane,
                                    acc, lds + wave * WL);
-    {
-        const int g = lane >> 4, r = lane & 15;
-#pragma unroll
-        for (int tt = 0; tt < TWW; ++tt)
-#pragma unroll
-            for (int hh = 0; hh < H; ++hh) {
-                const int c = g + 4 * hh;
-                if (c < N) red[(wave * N + c) * SEG + tt * kTileRows + r] = acc[tt][hh];
-            }
-    }
+    store_partials<N, TWW>(red, wave, lane, acc);
     __syncthreads();
 
     const int row0 = st * kSuperRows + tg * SEG;
@@ -122,30 +164,58 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
         return;
     }
 
-    // Segments of SEG consecutive threads hold one column's rows; blockDim is
-    // a multiple of 64 and SEG divides 64, so a segment never straddles a
-    // wave or an iteration.
-    for (int idx = threadIdx.x; idx < N * SEG; idx += blockDim.x) {
-        // every wave's partial is read before the first add (clamped indices,
-        // adds in wave order): one LDS round trip instead of one per batch
-        const int c = idx / SEG, lr = idx % SEG;
-        float part[kMaxKsplit];
+    finish_rows<N, TWW>(red, ksplit, tscale, rows, row0, Y,
+                        MODE == kArgmax ? amax_ws + int64_t(blockIdx.x) * N : nullptr);
+}
+
+// ------------------------------------------------ several products, one launch
+
+// Up to kMaxBatch independent products of one activation matrix in one
+// launch (see nvfp4_gemv_batch): workgroups [group0, next group0) belong to a
+// product, and each runs exactly the narrow_kernel workgroup of that product
+// (the same waves, octet ranges and arithmetic), so every product has the
+// bits of its own nvfp4_gemv or nvfp4_gemv_argmax call.
+constexpr int kMaxBatch = 4;
+struct BatchSegment {
+    const uint8_t *wq, *ws;
+    float *Y;                    // NULL: not stored
+    unsigned long long *keys;    // NULL: no argmax; else the product's key slots
+    float tscale;
+    int rows;
+    int group0;                  // the product's first workgroup
+};
+struct BatchArgs {
+    BatchSegment seg[kMaxBatch];
+    int count;
+};
+
+template <int N, int TWW>
+__global__ void __launch_bounds__(kLanes * kMaxKsplit)
+narrow_batch_kernel(BatchArgs args, int octets, int kb, int ksplit, const uint16_t *__restrict__ X, int K) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int GPS = kSuperTiles / TWW;
+    constexpr int SEG = TWW * kTileRows;
+    constexpr int H = N > 4 ? 2 : 1;
+    // The workgroup's product, chosen with constant indices only (no
+    // indexing of the argument array in registers).
+    BatchSegment seg = args.seg[0];
 #pragma unroll
-        for (int w = 0; w < kMaxKsplit; ++w) part[w] = red[((w < ksplit ? w : 0) * N + c) * SEG + lr];
-        float tot = part[0];
-#pragma unroll
-        for (int w = 1; w < kMaxKsplit; ++w)
-            if (w < ksplit) tot += part[w];
-        const float y = tot * tscale;
-        const int row = row0 + lr;
-        const bool valid = row < rows;
-        if (valid && Y) Y[int64_t(c) * rows + row] = y;
-        if (MODE == kArgmax) {
-            // the segment's SEG lanes are all active (SEG divides 64)
-            const unsigned long long key = lanes_max_u64<SEG>(valid ? argmax_key(y, uint32_t(row)) : 0ull);
-            if (lr == 0) amax_ws[int64_t(blockIdx.x) * N + c] = key;
-        }
-    }
+    for (int i = 1; i < kMaxBatch; ++i)
+        if (i < args.count && int(blockIdx.x) >= args.seg[i].group0) seg = args.seg[i];
+    const int b = int(blockIdx.x) - seg.group0;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int st = b / GPS, tg = b % GPS;
+    const int o0 = int(int64_t(octets) * wave / ksplit), o1 = int(int64_t(octets) * (wave + 1) / ksplit);
+    constexpr int WL = narrow_wave_lds_bytes(N);
+    float *const red = reinterpret_cast<float *>(lds + int(blockDim.x >> 6) * WL);
+    float acc[TWW][H];
+    narrow_accumulate<N, TWW, kNvfp4>(seg.wq, seg.ws, int64_t(st), tg, o0, o1, octets, kb, X, K, lane, acc,
+                                      lds + wave * WL);
+    store_partials<N, TWW>(red, wave, lane, acc);
+    __syncthreads();
+    finish_rows<N, TWW>(red, ksplit, seg.tscale, seg.rows, st * kSuperRows + tg * SEG, seg.Y,
+                        seg.keys ? seg.keys + int64_t(b) * N : nullptr);
 }
 
 // Second launch of the argmax: the product's per-workgroup keys are complete
@@ -356,14 +426,8 @@ NVFP4_API size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, i
     return size_t(narrow_config(Geometry(rows, cols), n).groups) * size_t(n) * sizeof(unsigned long long);
 }
 
-// The argmax's two launches with `keys` as the product's workspace; the
-// arguments are already validated.
-static int launch_gemv_argmax(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale,
-                              const uint16_t *X, int n, float *logits, int32_t *argmax, unsigned long long *keys,
-                              hipStream_t stream) {
-    (void)hipGetLastError();
-    if (int st = launch_narrow<kArgmax>(g, wq, ws, tscale, X, n, logits, keys, stream)) return st;
-    const int groups = int(narrow_config(g, n).groups);
+// The argmax finish of `groups` workgroups' keys of n columns.
+static int launch_finish(int n, const unsigned long long *keys, int groups, int32_t *argmax, hipStream_t stream) {
 #define NVFP4_FINISH(NN) \
     hipLaunchKernelGGL(argmax_finish_kernel<NN>, dim3(1), dim3(kFinishThreads), 0, stream, keys, groups, argmax)
     switch (n) {
@@ -378,6 +442,16 @@ static int launch_gemv_argmax(const Geometry &g, const uint8_t *wq, const uint8_
     }
 #undef NVFP4_FINISH
     return launch_status();
+}
+
+// The argmax's two launches with `keys` as the product's workspace; the
+// arguments are already validated.
+static int launch_gemv_argmax(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale,
+                              const uint16_t *X, int n, float *logits, int32_t *argmax, unsigned long long *keys,
+                              hipStream_t stream) {
+    (void)hipGetLastError();
+    if (int st = launch_narrow<kArgmax>(g, wq, ws, tscale, X, n, logits, keys, stream)) return st;
+    return launch_finish(n, keys, int(narrow_config(g, n).groups), argmax, stream);
 }
 
 static int check_argmax_args(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
@@ -474,4 +548,131 @@ NVFP4_API int mxfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int
     (void)hipGetLastError();
     if (n <= kMaxNarrowN) return launch_narrow_mx(g, wq, ws, tscale, X, n, Y, stream);
     return launch_mfma(g, wq, ws, tscale, X, n, Y, stream, kMxfp4);
+}
+
+// --------------------------------------------------- several products, one launch
+
+namespace {
+
+// How nvfp4_gemv_batch runs a batch: one launch of narrow_batch_kernel when
+// every product's own decomposition splits a row over the same number of
+// waves (then each product's bits are those of its own call, whatever the
+// tiles per workgroup), with the largest of the products' tiles per
+// workgroup; otherwise each product's own launch.  Keys of the argmax
+// products follow one another in the workspace.
+struct BatchPlan {
+    bool fused;
+    int ksplit, tww;
+    int64_t groups[kMaxBatch];      // workgroups of each product
+    int64_t key_offset[kMaxBatch];  // first key of each argmax product (in keys)
+    int64_t keys;                   // keys in all
+    int64_t total_groups;
+};
+
+BatchPlan plan_batch(const nvfp4_product *p, int count, int64_t cols, int n) {
+    BatchPlan b{};
+    b.fused = count > 1;
+    for (int i = 0; i < count; ++i) {
+        const NarrowConfig c = narrow_config(Geometry(p[i].rows, cols), n);
+        if (i == 0) {
+            b.ksplit = c.ksplit;
+            b.tww = c.tww;
+        }
+        if (c.ksplit != b.ksplit) b.fused = false;
+        if (c.tww > b.tww) b.tww = c.tww;
+    }
+    for (int i = 0; i < count; ++i) {
+        const Geometry g(p[i].rows, cols);
+        b.groups[i] = b.fused ? g.supertiles * (kSuperTiles / b.tww) : narrow_config(g, n).groups;
+        b.key_offset[i] = b.keys;
+        if (p[i].argmax) b.keys += b.groups[i] * n;
+        b.total_groups += b.groups[i];
+    }
+    return b;
+}
+
+int check_batch(const nvfp4_product *p, int count, int64_t cols, int n) {
+    if (!p || count < 1 || count > kMaxBatch || n < 1 || n > kMaxNarrowN) return NVFP4_EINVAL;
+    if (int st = check_shape(1, cols)) return st;
+    if (cols > kMaxNarrowCols) return NVFP4_ESHAPE;
+    for (int i = 0; i < count; ++i) {
+        const nvfp4_product &q = p[i];
+        if (!q.wq || !q.ws || !tscale_ok(q.tscale) || (!q.y && !q.argmax)) return NVFP4_EINVAL;
+        if (int st = check_shape(q.rows, cols)) return st;
+        if (!aligned(q.wq, 16) || !aligned(q.ws, 16) || !aligned(q.y, 4) || !aligned(q.argmax, 4)) return NVFP4_EALIGN;
+    }
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+NVFP4_API size_t nvfp4_gemv_batch_workspace_bytes(const nvfp4_product *products, int count, int64_t cols, int n) {
+    if (check_batch(products, count, cols, n) != NVFP4_OK) return 0;
+    return size_t(plan_batch(products, count, cols, n).keys) * sizeof(unsigned long long);
+}
+
+NVFP4_API int nvfp4_gemv_batch(const nvfp4_product *products, int count, int64_t cols, const uint16_t *X, int n,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!X) return NVFP4_EINVAL;
+    if (int st = check_batch(products, count, cols, n)) return st;
+    if (!aligned(X, 16)) return NVFP4_EALIGN;
+    const BatchPlan b = plan_batch(products, count, cols, n);
+    if (b.keys > 0) {
+        if (!workspace) return NVFP4_EINVAL;
+        if (!aligned(workspace, 8)) return NVFP4_EALIGN;
+        if (workspace_bytes < size_t(b.keys) * sizeof(unsigned long long)) return NVFP4_EWORKSPACE;
+    }
+    if (b.total_groups > (int64_t(1) << 31) - 1) return NVFP4_ESHAPE;
+    auto *keys = static_cast<unsigned long long *>(workspace);
+    (void)hipGetLastError();
+    if (b.fused) {
+        BatchArgs a{};
+        a.count = count;
+        int64_t g0 = 0;
+        for (int i = 0; i < count; ++i) {
+            const nvfp4_product &q = products[i];
+            a.seg[i] = BatchSegment{q.wq, q.ws, q.y, q.argmax ? keys + b.key_offset[i] : nullptr, q.tscale,
+                                    int(q.rows), int(g0)};
+            g0 += b.groups[i];
+        }
+        const Geometry g(1, cols);
+        const size_t lds = narrow_lds_bytes(b.ksplit, n, b.tww);
+        if (lds > kNarrowLdsLimit) return NVFP4_EINVAL;
+        const dim3 grid{unsigned(b.total_groups)}, block{unsigned(kLanes * b.ksplit)};
+        const int octets = int(g.octets), kb = int(g.kb), K = int(cols);
+#define NVFP4_BATCH(NN, TT) \
+    hipLaunchKernelGGL((narrow_batch_kernel<NN, TT>), grid, block, lds, stream, a, octets, kb, b.ksplit, X, K)
+#define NVFP4_BATCH_N(TT)                    \
+    switch (n) {                            \
+        case 1: NVFP4_BATCH(1, TT); break;  \
+        case 2: NVFP4_BATCH(2, TT); break;  \
+        case 3: NVFP4_BATCH(3, TT); break;  \
+        case 4: NVFP4_BATCH(4, TT); break;  \
+        case 5: NVFP4_BATCH(5, TT); break;  \
+        case 6: NVFP4_BATCH(6, TT); break;  \
+        case 7: NVFP4_BATCH(7, TT); break;  \
+        default: NVFP4_BATCH(8, TT); break; \
+    }
+        switch (b.tww) {
+            case 1: NVFP4_BATCH_N(1); break;
+            case 2: NVFP4_BATCH_N(2); break;
+            default: NVFP4_BATCH_N(4); break;
+        }
+#undef NVFP4_BATCH_N
+#undef NVFP4_BATCH
+        if (int st = launch_status()) return st;
+    } else {
+        for (int i = 0; i < count; ++i) {
+            const nvfp4_product &q = products[i];
+            const Geometry g(q.rows, cols);
+            const int st = q.argmax ? launch_narrow<kArgmax>(g, q.wq, q.ws, q.tscale, X, n, q.y, keys + b.key_offset[i], stream)
+                                    : launch_narrow<kPlain>(g, q.wq, q.ws, q.tscale, X, n, q.y, nullptr, stream);
+            if (st) return st;
+        }
+    }
+    for (int i = 0; i < count; ++i)
+        if (products[i].argmax)
+            if (int st = launch_finish(n, keys + b.key_offset[i], int(b.groups[i]), products[i].argmax, stream))
+                return st;
+    return NVFP4_OK;
 }

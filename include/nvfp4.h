@@ -186,6 +186,44 @@ int nvfp4_gemv_argmax_noalloc(const uint8_t *wq, const uint8_t *ws, float tscale
                               int64_t cols, const uint16_t *X, int n, float *logits, int32_t *argmax,
                               hipStream_t stream);
 
+/* ---------------------------------------------------- a batch of products
+ * Several independent products of one activation matrix X [n][cols] in one
+ * launch: the bw24 wiki's MTP item verifies K+1 draft tokens in one batched
+ * forward, whose products of one input (the vocabulary head beside another
+ * projection of the same hidden state, or the projections that share a
+ * layer's input) need not wait for one another.  Product i computes
+ * y = W_i X as nvfp4_gemv does (y may be NULL when argmax is set), and, with
+ * argmax set, the per-column greedy index as nvfp4_gemv_argmax does.  Every
+ * product's outputs are bit for bit those of its own call. */
+typedef struct nvfp4_product {
+    const uint8_t *wq;     /* repacked code plane (16-byte aligned) */
+    const uint8_t *ws;     /* repacked scale plane (16-byte aligned) */
+    float tscale;          /* fp32 tensor scale, finite and > 0 */
+    int64_t rows;          /* output rows of W_i */
+    float *y;              /* fp32 [n][rows], 4-byte aligned; NULL: not stored (argmax set) */
+    int32_t *argmax;       /* NULL: a plain product; else int32 [n] greedy rows */
+} nvfp4_product;
+
+/* Largest batch of nvfp4_gemv_batch. */
+#define NVFP4_MAX_BATCH 4
+
+/* Workspace bytes of nvfp4_gemv_batch: the argmax products' keys, one 64-bit
+ * key per workgroup and column (0 when no product has argmax set, or for
+ * invalid arguments). */
+size_t nvfp4_gemv_batch_workspace_bytes(const nvfp4_product *products, int count, int64_t cols, int n);
+
+/* The products of `count` (1..NVFP4_MAX_BATCH) matrices of `cols` columns
+ * with the same X (bf16 bits [n][cols], 1 <= n <= 8): one product launch
+ * when the matrices' own decompositions split a row over the same number of
+ * waves (true for the 17408 x 5120 matrix beside the 151936 x 5120
+ * vocabulary head), else one launch per product; then one argmax finish per
+ * argmax product.  workspace: nvfp4_gemv_batch_workspace_bytes bytes,
+ * 8-byte aligned, any contents (NULL allowed when no argmax is asked).
+ * Errors as nvfp4_gemv / nvfp4_gemv_argmax; NVFP4_EINVAL also for a count
+ * out of range or a product with neither y nor argmax. */
+int nvfp4_gemv_batch(const nvfp4_product *products, int count, int64_t cols, const uint16_t *X, int n,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* SwiGLU between the MLP matvecs: gu fp32 [n][2F] holds the stacked gate
  * (columns 0..F-1) and up (F..2F-1) outputs; h [n][F] bf16 bits =
  * bf16_nearest_even(g * u / (1 + exp(-g))) computed in fp32 (the pages'

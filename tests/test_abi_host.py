@@ -275,3 +275,64 @@ def test_argmax_noalloc_validation(lib):
     assert g(A, B, 1.0, 16, 32, C, 4, NULL, NULL, S0) == EINVAL
     assert g(A, B, 1.0, 16, 32, C, 4, ctypes.c_void_p(0x300002), A, S0) == EALIGN
     assert g(MIS, B, 1.0, 16, 32, C, 4, NULL, A, S0) == EALIGN
+
+
+class _Prod(ctypes.Structure):
+    _fields_ = [("wq", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("tscale", ctypes.c_float),
+                ("rows", ctypes.c_int64), ("y", ctypes.c_void_p), ("argmax", ctypes.c_void_p)]
+
+
+def _prods(*items):
+    arr = (_Prod * len(items))()
+    for i, (rows, y, am) in enumerate(items):
+        arr[i] = _Prod(A, B, 1.0, rows, y, am)
+    return arr
+
+
+def test_batch_workspace_and_validation(lib):
+    lib.nvfp4_gemv_batch_workspace_bytes.restype = ctypes.c_size_t
+    lib.nvfp4_gemv_batch_workspace_bytes.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+    lib.nvfp4_gemv_batch.restype = ctypes.c_int
+    lib.nvfp4_gemv_batch.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    wsb = lib.nvfp4_gemv_batch_workspace_bytes
+    # the verify pair at n = 4 runs as one launch with two tiles per
+    # workgroup: the head's 2374 super-tiles give 4748 workgroups x 4 keys
+    pair = _prods((151936, C, A), (17408, C, NULL))
+    assert wsb(pair, 2, 5120, 4) == 4748 * 4 * 8
+    # no argmax: no workspace
+    assert wsb(_prods((4096, C, NULL)), 1, 4096, 1) == 0
+    # one launch at the larger product's two tiles per workgroup: the
+    # 9000-row product's 141 super-tiles give 282 workgroups, not its own 564
+    assert wsb(_prods((70000, C, A), (9000, C, A)), 2, 2048, 1) == (2188 + 282) * 8
+    # 8 against 16 waves a row: each product's own decomposition
+    mixed = _prods((9000, C, A), (700, C, A))
+    assert wsb(mixed, 2, 2048, 3) == (nv.nvfp4_gemv_argmax_workspace_bytes(9000, 2048, 3) +
+                                      nv.nvfp4_gemv_argmax_workspace_bytes(700, 2048, 3))
+    g = lib.nvfp4_gemv_batch
+    assert g(pair, 0, 5120, C, 4, B, 1 << 20, S0) == EINVAL            # count
+    assert g(pair, 5, 5120, C, 4, B, 1 << 20, S0) == EINVAL
+    assert g(pair, 2, 5120, C, 9, B, 1 << 20, S0) == EINVAL            # n > 8
+    assert g(pair, 2, 5120, NULL, 4, B, 1 << 20, S0) == EINVAL         # X
+    assert g(pair, 2, 5120, MIS, 4, B, 1 << 20, S0) == EALIGN
+    assert g(pair, 2, 5128, C, 4, B, 1 << 20, S0) == ESHAPE            # cols % 16
+    assert g(pair, 2, 5120, C, 4, B, 4748 * 4 * 8 - 1, S0) == EWORKSPACE
+    assert g(pair, 2, 5120, C, 4, NULL, 1 << 20, S0) == EINVAL         # workspace needed
+    assert g(_prods((64, NULL, NULL)), 1, 512, C, 1, NULL, 0, S0) == EINVAL   # neither y nor argmax
+    assert g(_prods((64, ctypes.c_void_p(0x300002), NULL)), 1, 512, C, 1, NULL, 0, S0) == EALIGN
+    assert g(_prods((0, C, NULL)), 1, 512, C, 1, NULL, 0, S0) == ESHAPE
+
+
+def test_binding_batch_checks_every_product(lib):
+    R, K, n = 64, 512, 2
+    wq, ws = _t(nv.nvfp4_repacked_code_bytes(R, K)), _t(nv.nvfp4_repacked_scale_bytes(R, K))
+    X = torch.zeros(n, K, dtype=torch.bfloat16)
+    ok = dict(wq=wq, ws=ws, tscale=1.0, rows=R, y=torch.zeros(n, R), argmax=None)
+    with pytest.raises(ValueError, match=r"products\[1\].ws holds"):
+        nv.nvfp4_gemv_batch([ok, dict(ok, ws=ws[:-1].contiguous())], K, X, n)
+    with pytest.raises(ValueError, match=r"products\[0\].argmax: dtype"):
+        nv.nvfp4_gemv_batch([dict(ok, argmax=torch.zeros(n, dtype=torch.int64))], K, X, n)
+    with pytest.raises(ValueError, match=r"products\[0\].y holds"):
+        nv.nvfp4_gemv_batch([dict(ok, y=torch.zeros(n, R - 1))], K, X, n)
+    with pytest.raises(ValueError, match="must be in GPU memory"):
+        nv.nvfp4_gemv_batch([ok], K, X, n)

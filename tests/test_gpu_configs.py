@@ -9,6 +9,7 @@ import torch
 
 import oracle
 from block_scaled_bit_nvfp4_amd import workloads as wl
+import block_scaled_bit_nvfp4_amd as nv
 from tests import _gpu as G
 
 pytestmark = pytest.mark.gpu
@@ -18,7 +19,6 @@ pytestmark = pytest.mark.gpu
 def _device():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-    import block_scaled_bit_nvfp4_amd as nv
     nv.load()
     yield
     torch.cuda.synchronize()
@@ -78,7 +78,6 @@ def test_decode_4096x4096_full(copy):
 def test_mlp_27b_decode_layer():
     w = wl.WORKLOADS["mlp_27b_decode"]
     gate_up, down = w.matrices
-    import block_scaled_bit_nvfp4_amd as nv
     X = wl.activations(1, gate_up.cols, seed=wl.seed_of(w.name, "x"), device=G.DEV)
     G.note("config mlp_27b_decode gate_up")
     W1, c1, s1, q1, ss1 = _matrix(w, gate_up)
@@ -139,6 +138,20 @@ def test_verify_vocab_with_full_argmax(name):
     G.assert_within_tolerance(logits.cpu().numpy(), Y2, S2, "lm_head logits")
     want = oracle.argmax_first(Y2)
     assert list(am.cpu().numpy()) == list(want)
+    # the benchmarked launch: both products in one nvfp4_gemv_batch call give
+    # the bits of the two calls above
+    G.note("config %s batched" % name)
+    yb = torch.full((n, mw.rows), float("nan"), dtype=torch.float32, device=G.DEV)
+    lb = torch.full((n, head.rows), float("nan"), dtype=torch.float32, device=G.DEV)
+    ab = torch.full((n,), -7, dtype=torch.int32, device=G.DEV)
+    prods = [dict(wq=q2, ws=ss2, tscale=w.tscale, rows=head.rows, y=lb, argmax=ab),
+             dict(wq=q1, ws=ss1, tscale=w.tscale, rows=mw.rows, y=yb)]
+    wsp = torch.empty(max(8, nv.nvfp4_gemv_batch_workspace_bytes(prods, mw.cols, n)), dtype=torch.uint8,
+                      device=G.DEV)
+    nv.nvfp4_gemv_batch(prods, mw.cols, X, n, wsp)
+    assert np.array_equal(yb.cpu().numpy().view(np.uint32), Y1.view(np.uint32))
+    assert torch.equal(lb.view(torch.int32), logits.view(torch.int32))
+    assert list(ab.cpu().numpy()) == list(want)
     # report how far the winner leads the runner-up next to the tolerance
     for c in range(n):
         order = np.argsort(Y2[c])
@@ -182,7 +195,6 @@ def test_draft_head_8192x4096_full_argmax():
 
 
 def _mx_matrix(workload, m, copy=0):
-    import block_scaled_bit_nvfp4_amd as nv
     W = wl.weights(m.rows, m.cols, seed=wl.seed_of(workload.name, m.name, copy),
                    outliers=workload.outliers, device=G.DEV)
     codes = torch.empty(m.rows, m.cols // 2, dtype=torch.uint8, device=G.DEV)
@@ -194,7 +206,6 @@ def _mx_matrix(workload, m, copy=0):
 
 
 def test_mxfp4_gemv_17408x5120_full():
-    import block_scaled_bit_nvfp4_amd as nv
     w = wl.WORKLOADS["mxfp4_gemv_17408x5120"]
     m = w.matrices[0]
     X = wl.activations(1, m.cols, seed=wl.seed_of(w.name, "x"), device=G.DEV)
@@ -211,7 +222,6 @@ def test_mxfp4_gemv_17408x5120_full():
 
 
 def test_mxfp4_prefill_n512_sampled():
-    import block_scaled_bit_nvfp4_amd as nv
     w = wl.WORKLOADS["mxfp4_prefill_n512"]
     m = w.matrices[0]
     X = wl.activations(512, m.cols, seed=wl.seed_of(w.name, "x"), device=G.DEV)
