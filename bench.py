@@ -523,10 +523,10 @@ def kernel_source_hash():
 
 
 def measured_traffic(workload, variant=None):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if absent, taken on different kernel sources, or taken
-    on another variant of the step (the counters were collected on the
-    default one)."""
+    """HBM bytes of one dominant call (its product kernel, plus the argmax
+    finish where the call has one) from the committed counter summary, or
+    None if absent, taken on different kernel sources, or taken on another
+    variant of the step (the counters were collected on the default one)."""
     if variant:
         return None
     p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
@@ -536,7 +536,7 @@ def measured_traffic(workload, variant=None):
         d = json.load(f)
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return d.get("bytes_per_launch")
+    return d.get("dominant_bytes_per_launch")
 
 
 # ------------------------------------------------------------- one config --
