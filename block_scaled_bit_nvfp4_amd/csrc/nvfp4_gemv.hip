@@ -120,7 +120,7 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
     const int st = blockIdx.x / GPS, tg = blockIdx.x % GPS;
     const int half = MODE == kSwiglu ? wave / ksplit : 0;
     const int part = MODE == kSwiglu ? wave % ksplit : wave;
-    const int o0 = int(int64_t(octets) * part / ksplit), o1 = int(int64_t(octets) * (part + 1) / ksplit);
+    const int o0 = octet_bound(octets, part, ksplit), o1 = octet_bound(octets, part + 1, ksplit);
     constexpr int WL = narrow_wave_lds_bytes(N);
     float *const red = reinterpret_cast<float *>(lds + int(blockDim.x >> 6) * WL);
 
@@ -182,11 +182,10 @@ struct BatchSegment {
     unsigned long long *keys;    // NULL: no argmax; else the product's key slots
     float tscale;
     int rows;
-    int group0;                  // the product's first workgroup
 };
 struct BatchArgs {
+    int group0[kMaxBatch];       // each product's first workgroup; unused entries past the last workgroup
     BatchSegment seg[kMaxBatch];
-    int count;
 };
 
 template <int N, int TWW>
@@ -196,17 +195,27 @@ narrow_batch_kernel(BatchArgs args, int octets, int kb, int ksplit, const uint16
     constexpr int GPS = kSuperTiles / TWW;
     constexpr int SEG = TWW * kTileRows;
     constexpr int H = N > 4 ? 2 : 1;
-    // The workgroup's product, chosen with constant indices only (no
-    // indexing of the argument array in registers).
-    BatchSegment seg = args.seg[0];
+    // The workgroup's product: the products' first workgroups and every
+    // other scalar argument come in one round of argument loads, then the
+    // product's fields in a second (a uniform index into the argument
+    // segment, no copy of the array to registers).  The empty asm statements
+    // keep the compiler from sinking loads into later, dependent rounds.
+    asm volatile("" ::"s"(X), "s"(K), "s"(octets), "s"(kb), "s"(ksplit));
+    int pi = 0, g0 = 0;   // group0[0] is 0
 #pragma unroll
     for (int i = 1; i < kMaxBatch; ++i)
-        if (i < args.count && int(blockIdx.x) >= args.seg[i].group0) seg = args.seg[i];
-    const int b = int(blockIdx.x) - seg.group0;
+        if (int(blockIdx.x) >= args.group0[i]) {   // ascending: the last one passed is the product's
+            pi = i;
+            g0 = args.group0[i];
+        }
+    pi = __builtin_amdgcn_readfirstlane(pi);
+    const BatchSegment seg = args.seg[pi];
+    asm volatile("" ::"s"(seg.wq), "s"(seg.ws));
+    const int b = int(blockIdx.x) - g0;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int st = b / GPS, tg = b % GPS;
-    const int o0 = int(int64_t(octets) * wave / ksplit), o1 = int(int64_t(octets) * (wave + 1) / ksplit);
+    const int o0 = octet_bound(octets, wave, ksplit), o1 = octet_bound(octets, wave + 1, ksplit);
     constexpr int WL = narrow_wave_lds_bytes(N);
     float *const red = reinterpret_cast<float *>(lds + int(blockDim.x >> 6) * WL);
     float acc[TWW][H];
@@ -627,14 +636,15 @@ NVFP4_API int nvfp4_gemv_batch(const nvfp4_product *products, int count, int64_t
     (void)hipGetLastError();
     if (b.fused) {
         BatchArgs a{};
-        a.count = count;
         int64_t g0 = 0;
         for (int i = 0; i < count; ++i) {
             const nvfp4_product &q = products[i];
+            a.group0[i] = int(g0);
             a.seg[i] = BatchSegment{q.wq, q.ws, q.y, q.argmax ? keys + b.key_offset[i] : nullptr, q.tscale,
-                                    int(q.rows), int(g0)};
+                                    int(q.rows)};
             g0 += b.groups[i];
         }
+        for (int i = count; i < kMaxBatch; ++i) a.group0[i] = int(g0);   // past the grid: never selected
         const Geometry g(1, cols);
         const size_t lds = narrow_lds_bytes(b.ksplit, n, b.tww);
         if (lds > kNarrowLdsLimit) return NVFP4_EINVAL;

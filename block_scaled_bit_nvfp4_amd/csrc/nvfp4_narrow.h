@@ -107,6 +107,16 @@ inline NarrowConfig narrow_config(const Geometry &g, int n, int max_tww = 4) {
     return c;
 }
 
+// Octet range [o0, o1) of wave part p of ksplit over a row's octets.  The
+// narrow products take at most kMaxNarrowCols columns (2^19 octets) and 16
+// waves, so octets * (p + 1) < 2^23 and 32-bit unsigned division gives the
+// exact quotients (a 64-bit one expands into a long emulated sequence ahead
+// of the first load).
+__device__ __forceinline__ int octet_bound(int octets, int p, int ksplit) {
+    return int(uint32_t(octets) * uint32_t(p) / uint32_t(ksplit));
+}
+static_assert((kMaxNarrowCols / (kOctet * kBlock)) * kMaxKsplit < (int64_t(1) << 32), "octet bounds fit 32 bits");
+
 // Bytes of LDS per wave of the narrow kernels: a 256-byte run of zeros, then
 // one slot of compact activations (1 KiB per four columns).
 constexpr int narrow_wave_lds_bytes(int n) { return 256 + (n > 4 ? 2 : 1) * 1024; }
