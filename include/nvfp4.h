@@ -219,8 +219,10 @@ size_t nvfp4_gemv_batch_workspace_bytes(const nvfp4_product *products, int count
  * vocabulary head), else one launch per product; then one argmax finish per
  * argmax product.  workspace: nvfp4_gemv_batch_workspace_bytes bytes,
  * 8-byte aligned, any contents (NULL allowed when no argmax is asked).
- * Errors as nvfp4_gemv / nvfp4_gemv_argmax; NVFP4_EINVAL also for a count
- * out of range or a product with neither y nor argmax. */
+ * The products' outputs must not overlap one another, X, the planes or the
+ * workspace (the launches write them concurrently).  Errors as nvfp4_gemv /
+ * nvfp4_gemv_argmax; NVFP4_EINVAL also for a count out of range or a
+ * product with neither y nor argmax. */
 int nvfp4_gemv_batch(const nvfp4_product *products, int count, int64_t cols, const uint16_t *X, int n,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
