@@ -350,6 +350,31 @@ int launch_narrow(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float
 
 int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
                 int n, float *Y, hipStream_t stream, int fmt = kNvfp4);
+bool wide_fills_device(const Geometry &g, int n, int fmt);
+
+// Products of 9..32 columns as passes of the matvec over column chunks of
+// at most eight (columns [8p, 8p + 8) of X and Y in pass p): each column then
+// has the bits of its one-column product, and the weights are read once per
+// pass.  The wide product costs the same from 9 to 128 columns (its
+// workgroups each decode their weights for a 128-column tile), so two passes
+// always beat it; three or four only where its workgroups do not fill the
+// CUs or cannot take the shape (17408 x 5120: 29 us for 16 columns in two
+// passes against 65 us).  Returns the number of passes, 0 for the wide
+// product.
+int narrow_passes(const Geometry &g, int n, int fmt) {
+    if (n <= kMaxNarrowN || n > 4 * kMaxNarrowN || g.cols > kMaxNarrowCols) return 0;
+    const int passes = int(ceil_div(n, kMaxNarrowN));
+    return passes <= 2 || !wide_fills_device(g, n, fmt) ? passes : 0;
+}
+
+template <typename Launch>
+int launch_passes(const Geometry &g, const uint16_t *X, int n, float *Y, Launch launch) {
+    for (int c0 = 0; c0 < n; c0 += kMaxNarrowN) {
+        const int w = n - c0 < kMaxNarrowN ? n - c0 : kMaxNarrowN;
+        if (int st = launch(X + int64_t(c0) * g.cols, w, Y + int64_t(c0) * g.rows)) return st;
+    }
+    return NVFP4_OK;
+}
 
 // The MXFP4 matvec: the plain product's decomposition and kernel with the
 // E8M0 scale plane, at most two tiles per workgroup.
@@ -426,6 +451,10 @@ NVFP4_API int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int
     const Geometry g(rows, cols);
     (void)hipGetLastError();
     if (n <= kMaxNarrowN) return launch_narrow<kPlain>(g, wq, ws, tscale, X, n, Y, nullptr, stream);
+    if (narrow_passes(g, n, kNvfp4))
+        return launch_passes(g, X, n, Y, [&](const uint16_t *Xp, int w, float *Yp) {
+            return launch_narrow<kPlain>(g, wq, ws, tscale, Xp, w, Yp, nullptr, stream);
+        });
     return launch_mfma(g, wq, ws, tscale, X, n, Y, stream);
 }
 
@@ -556,6 +585,10 @@ NVFP4_API int mxfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int
     const Geometry g(rows, cols);
     (void)hipGetLastError();
     if (n <= kMaxNarrowN) return launch_narrow_mx(g, wq, ws, tscale, X, n, Y, stream);
+    if (narrow_passes(g, n, kMxfp4))
+        return launch_passes(g, X, n, Y, [&](const uint16_t *Xp, int w, float *Yp) {
+            return launch_narrow_mx(g, wq, ws, tscale, Xp, w, Yp, stream);
+        });
     return launch_mfma(g, wq, ws, tscale, X, n, Y, stream, kMxfp4);
 }
 

@@ -490,6 +490,15 @@ static const WideDevice *wide_device() {
     return &w;
 }
 
+// True when the wide product takes the shape and its workgroups at n
+// columns are at least the device's CUs (false where the device cannot be
+// queried).
+bool wide_fills_device(const Geometry &g, int n, int fmt) {
+    if (g.cols > kMaxWideCols || int64_t(g.scale_bytes(fmt)) > kMaxWideScaleBytes) return false;
+    const WideDevice *wd = wide_device();
+    return wd && wide_config(g, n, wd->cus).groups >= wd->cus;
+}
+
 int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
                 int n, float *Y, hipStream_t stream, int fmt) {
     if (g.cols > kMaxWideCols || int64_t(g.scale_bytes(fmt)) > kMaxWideScaleBytes) return NVFP4_ESHAPE;

@@ -1,8 +1,8 @@
 """GPU parity at the largest shapes the products accept: rows of 2^26
-elements for the n <= 8 matvec (its 32-bit buffer offsets reach 2^31 bytes
-per super-tile stream) and of 2^22 elements for the wide contraction, in
-both formats; one block past either limit is rejected on the host
-(tests/test_abi_host.py)."""
+elements for the matvec (n <= 8, and its passes over 9..32 columns; its
+32-bit buffer offsets reach 2^31 bytes per super-tile stream) and of 2^22
+elements for the wide contraction, in both formats; one block past either
+limit is rejected on the host (tests/test_abi_host.py)."""
 import numpy as np
 import pytest
 import torch
@@ -60,6 +60,14 @@ def test_narrow_at_max_cols(fmt, n):
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_matvec_passes_at_max_cols(fmt):
+    """Ten columns: two passes of the matvec, the second reading X and
+    writing Y 8 rows in (an offset of 2^30 bytes into X)."""
+    G.note("limits passes %s 1x%d n=10" % (fmt, MAX_NARROW_COLS))
+    _run(fmt, 1, MAX_NARROW_COLS, 10, 111)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 def test_wide_at_max_cols(fmt):
-    G.note("limits wide %s 16x%d n=16" % (fmt, MAX_WIDE_COLS))
-    _run(fmt, 16, MAX_WIDE_COLS, 16, 201)
+    G.note("limits wide %s 16x%d n=33" % (fmt, MAX_WIDE_COLS))
+    _run(fmt, 16, MAX_WIDE_COLS, 33, 201)

@@ -239,6 +239,41 @@ def test_gemv_deterministic_and_column_identity(R, K):
         assert [int(v) for v in am.cpu().numpy()] == single_am[:n], n
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("R,K", [
+    (17408, 5120),   # the wide product's workgroups leave CUs idle: passes up to 32 columns
+    (1000, 2080),    # ragged rows and octets
+])
+def test_matvec_passes_column_identity(fmt, R, K):
+    """9..32 columns run as passes of the matvec where they are faster than
+    the wide product (always up to 16): column c then has the bits of the
+    one-column product of X[c], and every output is within the parity
+    tolerance of the oracle."""
+    mx = fmt == "mxfp4"
+    W = G.seeded_matrix(R, K, 31)
+    if mx:
+        codes = torch.empty(R, K // 2, dtype=torch.uint8, device=G.DEV)
+        scales = torch.empty(R, K // 32, dtype=torch.uint8, device=G.DEV)
+        nv.mxfp4_quantize(W, R, K, 1.0, codes, scales)
+        wq, ws = nv.alloc_mx_repacked(R, K, G.DEV)
+        nv.mxfp4_repack(codes, scales, R, K, wq, ws)
+        c_ref, s_ref = oracle.mx_quantize(W.cpu().numpy(), 1.0)
+    else:
+        wq, ws, c_ref, s_ref = _prepare(R, K, 31)
+    f = nv.mxfp4_gemv if mx else nv.nvfp4_gemv
+    X = G.seeded_x(32, K, seed=32)
+    singles = torch.full((32, R), float("nan"), dtype=torch.float32, device=G.DEV)
+    for c in range(32):
+        f(wq, ws, 0.5, R, K, X[c:c + 1].contiguous(), 1, singles[c:c + 1])
+    for n in (9, 12, 16) if R < 10000 else (9, 16, 17, 24, 32):
+        G.note("passes %s %dx%d n=%d" % (fmt, R, K, n))
+        y = torch.full((n, R), float("nan"), dtype=torch.float32, device=G.DEV)
+        f(wq, ws, 0.5, R, K, X[:n].contiguous(), n, y)
+        assert torch.equal(y.view(torch.int32), singles[:n].view(torch.int32)), n
+    Y_ref, S = (oracle.mx_gemv if mx else oracle.gemv)(c_ref, s_ref, 0.5, G.wl.bf16_bits(X[:16]))
+    G.assert_within_tolerance(singles[:16].cpu().numpy(), Y_ref, S, "passes %s %dx%d" % (fmt, R, K))
+
+
 # -------------------------------------------------------------- argmax, exact
 
 @pytest.mark.parametrize("R,K,n", [
