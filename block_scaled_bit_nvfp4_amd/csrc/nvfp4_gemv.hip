@@ -337,7 +337,7 @@ int launch_narrow_tww(const Geometry &g, const NarrowConfig &cfg, const uint8_t 
 template <int MODE>
 int launch_narrow(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
                   int n, float *Y, unsigned long long *amax_ws, hipStream_t stream) {
-    const NarrowConfig cfg = narrow_config(g, n);
+    const NarrowConfig cfg = MODE == kArgmax ? argmax_config(g, n) : narrow_config(g, n);
     switch (cfg.tww) {
         case 1: return launch_narrow_tww<MODE, 1>(g, cfg, wq, ws, tscale, X, n, Y, amax_ws, 0, nullptr, cfg.ksplit,
                                                  cfg.groups, stream);
@@ -461,7 +461,7 @@ NVFP4_API int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int
 NVFP4_API size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, int n) {
     // One 64-bit key per workgroup and column.
     if (n < 1 || n > kMaxNarrowN || check_shape(rows, cols) != NVFP4_OK || cols > kMaxNarrowCols) return 0;
-    return size_t(narrow_config(Geometry(rows, cols), n).groups) * size_t(n) * sizeof(unsigned long long);
+    return size_t(argmax_config(Geometry(rows, cols), n).groups) * size_t(n) * sizeof(unsigned long long);
 }
 
 // The argmax finish of `groups` workgroups' keys of n columns.
@@ -489,7 +489,7 @@ static int launch_gemv_argmax(const Geometry &g, const uint8_t *wq, const uint8_
                               hipStream_t stream) {
     (void)hipGetLastError();
     if (int st = launch_narrow<kArgmax>(g, wq, ws, tscale, X, n, logits, keys, stream)) return st;
-    return launch_finish(n, keys, int(narrow_config(g, n).groups), argmax, stream);
+    return launch_finish(n, keys, int(argmax_config(g, n).groups), argmax, stream);
 }
 
 static int check_argmax_args(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
@@ -615,7 +615,8 @@ BatchPlan plan_batch(const nvfp4_product *p, int count, int64_t cols, int n) {
     BatchPlan b{};
     b.fused = count > 1;
     for (int i = 0; i < count; ++i) {
-        const NarrowConfig c = narrow_config(Geometry(p[i].rows, cols), n);
+        const Geometry g(p[i].rows, cols);
+        const NarrowConfig c = p[i].argmax ? argmax_config(g, n) : narrow_config(g, n);
         if (i == 0) {
             b.ksplit = c.ksplit;
             b.tww = c.tww;
@@ -625,7 +626,8 @@ BatchPlan plan_batch(const nvfp4_product *p, int count, int64_t cols, int n) {
     }
     for (int i = 0; i < count; ++i) {
         const Geometry g(p[i].rows, cols);
-        b.groups[i] = b.fused ? g.supertiles * (kSuperTiles / b.tww) : narrow_config(g, n).groups;
+        b.groups[i] = b.fused ? g.supertiles * (kSuperTiles / b.tww)
+                              : (p[i].argmax ? argmax_config(g, n) : narrow_config(g, n)).groups;
         b.key_offset[i] = b.keys;
         if (p[i].argmax) b.keys += b.groups[i] * n;
         b.total_groups += b.groups[i];

@@ -107,6 +107,24 @@ inline NarrowConfig narrow_config(const Geometry &g, int n, int max_tww = 4) {
     return c;
 }
 
+// The argmax products' decomposition: one key per workgroup and column goes
+// to the finish launch, and at four columns a large matrix (more than 4096
+// tiles) takes four tiles per workgroup, as it does past four columns: half
+// the keys.  The 151936 x 5120 vocabulary head's call measured 75.3-76.0
+// against 76.0-79.0 us (its product alone 1.6 us slower, the finish faster),
+// the verify step with it 82.1-83.2 against 83.6-85.4 us; at one to three
+// columns four tiles measured no better (one column: 72 against 70 us).
+// Tiles per workgroup change no row's summation order, so the logits keep
+// the bits of the plain product.
+inline NarrowConfig argmax_config(const Geometry &g, int n) {
+    NarrowConfig c = narrow_config(g, n);
+    if (n == 4 && g.tiles > 4096 && c.tww < 4) {
+        c.tww = 4;
+        c.groups = g.supertiles;
+    }
+    return c;
+}
+
 // Octet range [o0, o1) of wave part p of ksplit over a row's octets.  The
 // narrow products take at most kMaxNarrowCols columns (2^19 octets) and 16
 // waves, so octets * (p + 1) < 2^23 and 32-bit unsigned division gives the

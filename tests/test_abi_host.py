@@ -73,10 +73,15 @@ def test_plane_sizes_invalid(lib, rows, cols):
 def test_workspace_bytes(lib):
     # one 64-bit key per workgroup and column: a 16 x 32 matrix runs 4
     # one-tile workgroups (its 64-row super-tile), the 151936 x 5120 vocabulary
-    # projection (9496 tiles) 4748 two-tile workgroups, the 17408 x 5120
-    # matrix (1088 tiles) 1088 one-tile workgroups
+    # projection (9496 tiles) 4748 two-tile workgroups at one to three
+    # columns and, from four columns (the argmax's own rule at four), 2374
+    # four-tile ones; the 17408 x 5120 matrix (1088 tiles) 1088 one-tile
+    # workgroups
     assert [nv.nvfp4_gemv_argmax_workspace_bytes(16, 32, n) for n in (0, 1, 4, 8, 9)] == [0, 32, 128, 256, 0]
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 4) == 4748 * 4 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 1) == 4748 * 1 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 3) == 4748 * 3 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 4) == 2374 * 4 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 4) == 1088 * 4 * 8     # 1088 tiles: one each
     assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 1) == 1088 * 8
     # 257..512 tiles: one tile per workgroup while a row has at most 32
     # octets (the 8192 x 4096 draft head), two tiles otherwise
@@ -299,10 +304,10 @@ def test_batch_workspace_and_validation(lib):
     lib.nvfp4_gemv_batch.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     wsb = lib.nvfp4_gemv_batch_workspace_bytes
-    # the verify pair at n = 4 runs as one launch with two tiles per
-    # workgroup: the head's 2374 super-tiles give 4748 workgroups x 4 keys
+    # the verify pair at n = 4 runs as one launch with the argmax head's four
+    # tiles per workgroup: its 2374 super-tiles give 2374 workgroups x 4 keys
     pair = _prods((151936, C, A), (17408, C, NULL))
-    assert wsb(pair, 2, 5120, 4) == 4748 * 4 * 8
+    assert wsb(pair, 2, 5120, 4) == 2374 * 4 * 8
     # no argmax: no workspace
     assert wsb(_prods((4096, C, NULL)), 1, 4096, 1) == 0
     # one launch at the larger product's two tiles per workgroup: the
@@ -319,7 +324,7 @@ def test_batch_workspace_and_validation(lib):
     assert g(pair, 2, 5120, NULL, 4, B, 1 << 20, S0) == EINVAL         # X
     assert g(pair, 2, 5120, MIS, 4, B, 1 << 20, S0) == EALIGN
     assert g(pair, 2, 5128, C, 4, B, 1 << 20, S0) == ESHAPE            # cols % 16
-    assert g(pair, 2, 5120, C, 4, B, 4748 * 4 * 8 - 1, S0) == EWORKSPACE
+    assert g(pair, 2, 5120, C, 4, B, 2374 * 4 * 8 - 1, S0) == EWORKSPACE
     assert g(pair, 2, 5120, C, 4, NULL, 1 << 20, S0) == EINVAL         # workspace needed
     assert g(_prods((64, NULL, NULL)), 1, 512, C, 1, NULL, 0, S0) == EINVAL   # neither y nor argmax
     assert g(_prods((64, ctypes.c_void_p(0x300002), NULL)), 1, 512, C, 1, NULL, 0, S0) == EALIGN
