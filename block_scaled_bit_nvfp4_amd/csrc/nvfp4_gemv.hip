@@ -41,6 +41,21 @@ __global__ void __launch_bounds__(256) swiglu_kernel(const float *__restrict__ g
     h[i] = uint16_t(bf16_rne_bits(swiglu_f32(gu[n * 2 * F + c], gu[n * 2 * F + F + c])));
 }
 
+// ------------------------------------------------- the argmax workspace
+
+// One argmax product's workspace: a finish header, then the keys
+// [workgroups][N] of the product.  The header holds the split finish's
+// counter (a 128-byte line of its own) and its workgroups' partial maxima
+// [kFinishGroups][N].  The product's first workgroup zeroes the counter, so
+// the workspace takes any contents and no clearing between calls.
+constexpr int kFinishGroups = 16;                  // workgroups of the split finish
+constexpr int kFinishCounterWords = 16;            // 128 bytes
+constexpr int64_t kFinishHeaderWords = kFinishCounterWords + kFinishGroups * kMaxNarrowN;
+
+__device__ __forceinline__ unsigned *finish_counter(unsigned long long *keys) {
+    return reinterpret_cast<unsigned *>(keys - kFinishHeaderWords);
+}
+
 // ------------------------------------------------------------ the products
 
 // The epilogue of the narrow products.  LDS: each wave's slot
@@ -96,8 +111,10 @@ __device__ __forceinline__ void finish_rows(const float *red, int ksplit, float 
 
 // MODE kPlain:  Y[c][row] = tscale * sum.
 // MODE kArgmax: as kPlain (Y may be NULL) plus, per column, the largest
-//   argmax key of the workgroup's rows stored to amax_ws[blockIdx][c];
-//   argmax_finish_kernel, launched next on the stream, reduces them.
+//   argmax key of the workgroup's rows stored to amax_ws[blockIdx][c]
+//   (amax_ws: the keys after the finish header, whose counter workgroup 0
+//   zeroes); an argmax finish kernel, launched next on the stream, reduces
+//   them.
 // MODE kSwiglu: the workgroup's waves [0, ksplit) take gate rows, waves
 //   [ksplit, 2 ksplit) the up rows up_st super-tiles further down (the same
 //   positions of the stacked matrix); h[c][row] = bf16(SiLU(g) u) with
@@ -123,6 +140,7 @@ narrow_kernel(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, fl
     const int o0 = octet_bound(octets, part, ksplit), o1 = octet_bound(octets, part + 1, ksplit);
     constexpr int WL = narrow_wave_lds_bytes(N);
     float *const red = reinterpret_cast<float *>(lds + int(blockDim.x >> 6) * WL);
+    if (MODE == kArgmax && blockIdx.x == 0 && threadIdx.x == 0) *finish_counter(amax_ws) = 0u;
 
     float acc[TWW][H];
     narrow_accumulate<N, TWW, FMT>(wq, ws, int64_t(st) + (half ? up_st : 0), tg, o0, o1, octets, kb, X, K, lane,
@@ -179,7 +197,7 @@ constexpr int kMaxBatch = 4;
 struct BatchSegment {
     const uint8_t *wq, *ws;
     float *Y;                    // NULL: not stored
-    unsigned long long *keys;    // NULL: no argmax; else the product's key slots
+    unsigned long long *keys;    // NULL: no argmax; else the product's keys (after its finish header)
     float tscale;
     int rows;
 };
@@ -218,6 +236,7 @@ narrow_batch_kernel(BatchArgs args, int octets, int kb, int ksplit, const uint16
     const int o0 = octet_bound(octets, wave, ksplit), o1 = octet_bound(octets, wave + 1, ksplit);
     constexpr int WL = narrow_wave_lds_bytes(N);
     float *const red = reinterpret_cast<float *>(lds + int(blockDim.x >> 6) * WL);
+    if (seg.keys != nullptr && b == 0 && threadIdx.x == 0) *finish_counter(seg.keys) = 0u;
     float acc[TWW][H];
     narrow_accumulate<N, TWW, kNvfp4>(seg.wq, seg.ws, int64_t(st), tg, o0, o1, octets, kb, X, K, lane, acc,
                                       lds + wave * WL);
@@ -230,11 +249,14 @@ narrow_batch_kernel(BatchArgs args, int octets, int kb, int ksplit, const uint16
 // Second launch of the argmax: the product's per-workgroup keys are complete
 // (kernel boundary); the largest key of each column names its row.  The
 // maximum is order-independent, so the result is exact and reproducible.
-// The keys were just written from every XCD, so each read goes to memory:
-// every thread issues all its loads of a pass (up to 8 groups of N keys, or
-// 32 keys of one column at N = 8) before it compares any of them, which keeps
-// the reduction to one or two memory round trips for up to 8192 groups
-// instead of one per loop iteration.
+// The keys were just written from every XCD, so each read goes to memory,
+// and one CU takes them in at only about 30 GB/s.  Up to 6144 keys (12288 at
+// one or two columns; finish_split) one workgroup reads them all: every
+// thread issues all its loads of a pass (up to 8 groups of N keys, or 32 keys
+// of one column at N = 8) before it compares any of them, one or two memory
+// round trips instead of one per loop iteration.  Above that,
+// argmax_finish_split_kernel spreads the reads over kFinishGroups workgroups
+// (on as many CUs).
 constexpr int kFinishThreads = 1024;
 
 template <int N>
@@ -304,6 +326,76 @@ argmax_finish_kernel(const unsigned long long *__restrict__ keys, int groups, in
         for (int w = 1; w < kFinishThreads / kLanes; ++w) best = part[w][c] > best ? part[w][c] : best;
         argmax_out[c] = int32_t(0xFFFFFFFFu - uint32_t(best));
     }
+}
+
+// The split finish: workgroup w reduces its share of the groups to N
+// partial maxima and stores them to the header with device-coherent
+// (agent-scope atomic) stores, which write through the XCD's L2; its first
+// wave waits for their acknowledgement (vmcnt 0, the wait an agent-scope
+// release makes for such stores) and counts the workgroup on the header's
+// counter with an agent-scope add; the workgroup that counts last reads the
+// kFinishGroups x N parts with device-coherent loads and writes the indices.
+// Only the parts cross workgroups and none of them is written through a
+// non-coherent L2 line, so no L2 write-back or invalidate is needed (one per
+// workgroup measured a microsecond slower).  The product zeroed the counter.
+constexpr int kSplitFinishThreads = 256;
+
+template <int N>
+__global__ void __launch_bounds__(kSplitFinishThreads)
+argmax_finish_split_kernel(unsigned long long *__restrict__ keys, int groups, int32_t *__restrict__ argmax_out) {
+    __shared__ unsigned long long part[kSplitFinishThreads / kLanes][N];
+    __shared__ int last;
+    unsigned long long *const parts = keys - kFinishHeaderWords + kFinishCounterWords;
+    const int per = (groups + kFinishGroups - 1) / kFinishGroups;
+    const int g_lo = int(blockIdx.x) * per;
+    const int g_hi = groups - g_lo < per ? groups : g_lo + per;
+    constexpr int U = N > 4 ? 2 : 4;   // groups per thread per pass
+    unsigned long long m[N];
+#pragma unroll
+    for (int c = 0; c < N; ++c) m[c] = 0ull;
+    for (int g0 = g_lo; g0 < g_hi; g0 += kSplitFinishThreads * U) {
+        unsigned long long k[U][N];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int g = g0 + u * kSplitFinishThreads + int(threadIdx.x);
+#pragma unroll
+            for (int c = 0; c < N; ++c) k[u][c] = g < g_hi ? keys[int64_t(g) * N + c] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < N; ++c) m[c] = k[u][c] > m[c] ? k[u][c] : m[c];
+    }
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+        m[c] = lanes_max_u64<kLanes>(m[c]);
+        if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][c] = m[c];
+    }
+    __syncthreads();
+    if (threadIdx.x < kLanes) {   // wave 0: the N part stores, their wait and the count
+        if (threadIdx.x < N) {
+            const int c = threadIdx.x;
+            unsigned long long best = part[0][c];
+#pragma unroll
+            for (int w = 1; w < kSplitFinishThreads / kLanes; ++w) best = part[w][c] > best ? part[w][c] : best;
+            __hip_atomic_store(&parts[int(blockIdx.x) * N + c], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (threadIdx.x == 0)
+            last = __hip_atomic_fetch_add(finish_counter(keys), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   unsigned(kFinishGroups - 1);
+    }
+    __syncthreads();
+    if (!last || threadIdx.x >= N) return;
+    const int c = threadIdx.x;
+    unsigned long long p[kFinishGroups];
+#pragma unroll
+    for (int w = 0; w < kFinishGroups; ++w)
+        p[w] = __hip_atomic_load(&parts[w * N + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long best = p[0];
+#pragma unroll
+    for (int w = 1; w < kFinishGroups; ++w) best = p[w] > best ? p[w] : best;
+    argmax_out[c] = int32_t(0xFFFFFFFFu - uint32_t(best));
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -459,15 +551,29 @@ NVFP4_API int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int
 }
 
 NVFP4_API size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, int n) {
-    // One 64-bit key per workgroup and column.
+    // The finish header, then one 64-bit key per workgroup and column.
     if (n < 1 || n > kMaxNarrowN || check_shape(rows, cols) != NVFP4_OK || cols > kMaxNarrowCols) return 0;
-    return size_t(argmax_config(Geometry(rows, cols), n).groups) * size_t(n) * sizeof(unsigned long long);
+    return (size_t(kFinishHeaderWords) + size_t(argmax_config(Geometry(rows, cols), n).groups) * size_t(n)) *
+           sizeof(unsigned long long);
 }
 
-// The argmax finish of `groups` workgroups' keys of n columns.
-static int launch_finish(int n, const unsigned long long *keys, int groups, int32_t *argmax, hipStream_t stream) {
-#define NVFP4_FINISH(NN) \
-    hipLaunchKernelGGL(argmax_finish_kernel<NN>, dim3(1), dim3(kFinishThreads), 0, stream, keys, groups, argmax)
+// Whether the argmax finish of `groups` workgroups' keys of n columns runs
+// split.  Measured on the vocabulary head (9496 keys either way): at four
+// columns the split finish took 0.6 us less, at two 0.3 us more, where the
+// one workgroup's loads take fewer instructions per key; at eight (18992
+// keys) 1.8 us less.
+inline bool finish_split(int64_t groups, int n) { return groups * n > (n <= 2 ? 12288 : 6144); }
+
+// The argmax finish of `groups` workgroups' keys of n columns (keys: after
+// the product's finish header).
+static int launch_finish(int n, unsigned long long *keys, int groups, int32_t *argmax, hipStream_t stream) {
+    const bool split = finish_split(groups, n);
+#define NVFP4_FINISH(NN)                                                                                      \
+    if (split)                                                                                              \
+        hipLaunchKernelGGL(argmax_finish_split_kernel<NN>, dim3(kFinishGroups), dim3(kSplitFinishThreads), 0, \
+                           stream, keys, groups, argmax);                                                   \
+    else                                                                                                    \
+        hipLaunchKernelGGL(argmax_finish_kernel<NN>, dim3(1), dim3(kFinishThreads), 0, stream, keys, groups, argmax)
     switch (n) {
         case 1: NVFP4_FINISH(1); break;
         case 2: NVFP4_FINISH(2); break;
@@ -482,11 +588,12 @@ static int launch_finish(int n, const unsigned long long *keys, int groups, int3
     return launch_status();
 }
 
-// The argmax's two launches with `keys` as the product's workspace; the
-// arguments are already validated.
+// The argmax's two launches in `workspace` (its finish header, then the
+// keys); the arguments are already validated.
 static int launch_gemv_argmax(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale,
-                              const uint16_t *X, int n, float *logits, int32_t *argmax, unsigned long long *keys,
-                              hipStream_t stream) {
+                              const uint16_t *X, int n, float *logits, int32_t *argmax,
+                              unsigned long long *workspace, hipStream_t stream) {
+    unsigned long long *const keys = workspace + kFinishHeaderWords;
     (void)hipGetLastError();
     if (int st = launch_narrow<kArgmax>(g, wq, ws, tscale, X, n, logits, keys, stream)) return st;
     return launch_finish(n, keys, int(argmax_config(g, n).groups), argmax, stream);
@@ -547,9 +654,9 @@ NVFP4_API int nvfp4_gemv_argmax_noalloc(const uint8_t *wq, const uint8_t *ws, fl
                                         hipStream_t stream) {
     if (int st = check_argmax_args(wq, ws, tscale, rows, cols, X, n, logits, argmax)) return st;
     if (nvfp4_gemv_argmax_workspace_bytes(rows, cols, n) > NVFP4_ARGMAX_SCRATCH_BYTES) return NVFP4_EWORKSPACE;
-    unsigned long long *keys = scratch_on_current_device();
-    if (!keys) return NVFP4_EHIP;
-    return launch_gemv_argmax(Geometry(rows, cols), wq, ws, tscale, X, n, logits, argmax, keys, stream);
+    unsigned long long *const ptr = scratch_on_current_device();
+    if (!ptr) return NVFP4_EHIP;
+    return launch_gemv_argmax(Geometry(rows, cols), wq, ws, tscale, X, n, logits, argmax, ptr, stream);
 }
 
 NVFP4_API int nvfp4_gemv_swiglu(const uint8_t *wq_gu, const uint8_t *ws_gu, float tscale, int64_t hidden,
@@ -600,14 +707,14 @@ namespace {
 // every product's own decomposition splits a row over the same number of
 // waves (then each product's bits are those of its own call, whatever the
 // tiles per workgroup), with the largest of the products' tiles per
-// workgroup; otherwise each product's own launch.  Keys of the argmax
-// products follow one another in the workspace.
+// workgroup; otherwise each product's own launch.  The argmax products'
+// workspaces (finish header, then keys) follow one another.
 struct BatchPlan {
     bool fused;
     int ksplit, tww;
     int64_t groups[kMaxBatch];      // workgroups of each product
-    int64_t key_offset[kMaxBatch];  // first key of each argmax product (in keys)
-    int64_t keys;                   // keys in all
+    int64_t key_offset[kMaxBatch];  // first key of each argmax product, after its finish header (words)
+    int64_t keys;                   // 64-bit words in all: each argmax product's header and keys
     int64_t total_groups;
 };
 
@@ -628,8 +735,8 @@ BatchPlan plan_batch(const nvfp4_product *p, int count, int64_t cols, int n) {
         const Geometry g(p[i].rows, cols);
         b.groups[i] = b.fused ? g.supertiles * (kSuperTiles / b.tww)
                               : (p[i].argmax ? argmax_config(g, n) : narrow_config(g, n)).groups;
-        b.key_offset[i] = b.keys;
-        if (p[i].argmax) b.keys += b.groups[i] * n;
+        b.key_offset[i] = b.keys + kFinishHeaderWords;
+        if (p[i].argmax) b.keys += kFinishHeaderWords + b.groups[i] * n;
         b.total_groups += b.groups[i];
     }
     return b;

@@ -145,12 +145,13 @@ int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
                const uint16_t *X, int n, float *Y, hipStream_t stream);
 
 /* Workspace bytes nvfp4_gemv_argmax needs for a rows x cols matrix and n
- * columns: one 64-bit key per workgroup of the product and column (at most
- * 4 bytes per row, rows rounded up to a multiple of 64); 0 for an invalid
- * shape or n out of 1..8.  It takes the matrix shape as well as n because
- * the product's workgroup count follows the shape; a caller that sizes one
- * workspace for every call of a model uses its largest matrix and n = 8
- * (4 bytes per row bound that for every n). */
+ * columns: a 1152-byte header for the finish, then one 64-bit key per
+ * workgroup of the product and column (at most 4 bytes per row, rows rounded
+ * up to a multiple of 64); 0 for an invalid shape or n out of 1..8.  It
+ * takes the matrix shape as well as n because the product's workgroup count
+ * follows the shape; a caller that sizes one workspace for every call of a
+ * model uses its largest matrix and n = 8 (the header plus 4 bytes per row
+ * bound that for every n). */
 size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, int n);
 
 /* nvfp4_gemv for 1 <= n <= 8 plus, per column c, argmax[c] = the lowest row
@@ -159,8 +160,12 @@ size_t nvfp4_gemv_argmax_workspace_bytes(int64_t rows, int64_t cols, int n);
  * decode-argmax gate; qwentin README, "How it works": dense-argmax descent).
  * Two launches: the product, whose workgroups each store, per column, the
  * largest (order-preserving value key, complemented row) of their rows to the
- * workspace, then a one-workgroup kernel that reduces those keys to row
- * indices.  No atomics: the result is exact and the same on every run.
+ * workspace, then a finish that reduces those keys to row indices: one
+ * workgroup, or, above 6144 keys (12288 for n <= 2), 16 workgroups whose
+ * partial maxima meet in the workspace header, where the last of them to
+ * count itself on an atomic counter (zeroed by the product) reduces them.
+ * A maximum does not depend on the order of its operands, so the result is
+ * exact and the same on every run.
  * logits [n][rows] may be NULL (not stored).  workspace: device memory of at
  * least nvfp4_gemv_argmax_workspace_bytes(rows, cols, n) bytes, 8-byte
  * aligned, any contents; the call overwrites it.  Calls sharing a workspace
@@ -170,7 +175,8 @@ int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_
                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Largest workspace nvfp4_gemv_argmax_noalloc serves: 1 MiB, enough for
- * every n <= 8 up to 262144 rows (4 bytes per row bound the workspace). */
+ * every n <= 8 up to 262144 rows (at most 256 KiB and the header there) and,
+ * at n = 8, for up to 1047424 rows of more than 4096 16-row tiles. */
 #define NVFP4_ARGMAX_SCRATCH_BYTES (1u << 20)
 
 /* nvfp4_gemv_argmax without a workspace argument and without any allocation,
@@ -184,7 +190,8 @@ int nvfp4_gemv_argmax(const uint8_t *wq, const uint8_t *ws, float tscale, int64_
  * NVFP4_EHIP if the array's address cannot be found.  Every call on one GPU
  * shares its array: calls that may overlap on one GPU (several streams, or
  * several host threads) race and must be serialised by the caller.  The
- * array needs no clearing: each call writes every key it reads. */
+ * array needs no clearing: each call writes every key it reads and zeroes
+ * the finish's counter before the finish counts on it. */
 int nvfp4_gemv_argmax_noalloc(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows,
                               int64_t cols, const uint16_t *X, int n, float *logits, int32_t *argmax,
                               hipStream_t stream);
@@ -210,9 +217,9 @@ typedef struct nvfp4_product {
 /* Largest batch of nvfp4_gemv_batch. */
 #define NVFP4_MAX_BATCH 4
 
-/* Workspace bytes of nvfp4_gemv_batch: the argmax products' keys, one 64-bit
- * key per workgroup and column (0 when no product has argmax set, or for
- * invalid arguments). */
+/* Workspace bytes of nvfp4_gemv_batch: each argmax product's finish header
+ * (1152 bytes) and keys, one 64-bit key per workgroup and column (0 when no
+ * product has argmax set, or for invalid arguments). */
 size_t nvfp4_gemv_batch_workspace_bytes(const nvfp4_product *products, int count, int64_t cols, int n);
 
 /* The products of `count` (1..NVFP4_MAX_BATCH) matrices of `cols` columns

@@ -71,39 +71,61 @@ def test_plane_sizes_invalid(lib, rows, cols):
 
 
 def test_workspace_bytes(lib):
-    # one 64-bit key per workgroup and column: a 16 x 32 matrix runs 4
-    # one-tile workgroups (its 64-row super-tile), the 151936 x 5120 vocabulary
-    # projection (9496 tiles) 4748 two-tile workgroups at one to three
-    # columns and, from four columns (the argmax's own rule at four), 2374
-    # four-tile ones; the 17408 x 5120 matrix (1088 tiles) 1088 one-tile
-    # workgroups
-    assert [nv.nvfp4_gemv_argmax_workspace_bytes(16, 32, n) for n in (0, 1, 4, 8, 9)] == [0, 32, 128, 256, 0]
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 1) == 4748 * 1 * 8
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 3) == 4748 * 3 * 8
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 4) == 2374 * 4 * 8
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 4) == 1088 * 4 * 8     # 1088 tiles: one each
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 1) == 1088 * 8
+    # a 1152-byte header for the finish (a 128-byte counter line, then 16
+    # workgroups x 8 columns of partial maxima), then one 64-bit key per
+    # workgroup and column: a 16 x 32 matrix runs 4 one-tile workgroups (its
+    # 64-row super-tile), the 151936 x 5120 vocabulary projection (9496 tiles)
+    # 4748 two-tile workgroups at one to three columns and, from four columns
+    # (the argmax's own rule at four), 2374 four-tile ones; the 17408 x 5120
+    # matrix (1088 tiles) 1088 one-tile workgroups
+    H = 1152
+    assert [nv.nvfp4_gemv_argmax_workspace_bytes(16, 32, n) for n in (0, 1, 4, 8, 9)] == [0, H + 32, H + 128,
+                                                                                           H + 256, 0]
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 1) == H + 4748 * 1 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 3) == H + 4748 * 3 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 4) == H + 2374 * 4 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 4) == H + 1088 * 4 * 8     # 1088 tiles: one each
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 1) == H + 1088 * 8
     # 257..512 tiles: one tile per workgroup while a row has at most 32
     # octets (the 8192 x 4096 draft head), two tiles otherwise
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 4096, 1) == 512 * 8
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 5120, 1) == 256 * 8
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(5120, 17408, 1) == 160 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 4096, 1) == H + 512 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 5120, 1) == H + 256 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(5120, 17408, 1) == H + 160 * 8
     # the two-tile parity shapes: 261 tiles with 33-octet rows, and 4100 tiles
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(4176, 4112, 1) == 66 * 2 * 8
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(65600, 528, 1) == 1025 * 2 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(4176, 4112, 1) == H + 66 * 2 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(65600, 528, 1) == H + 1025 * 2 * 8
     # past four columns the tiles per workgroup double, except for small
     # matrices and the two-tile shapes of 257..512 tiles
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 5) == 2374 * 5 * 8
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 8) == 544 * 8 * 8
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 4096, 6) == 256 * 6 * 8
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(4096, 4096, 8) == 256 * 8 * 8
-    assert nv.nvfp4_gemv_argmax_workspace_bytes(5120, 17408, 8) == 160 * 8 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(151936, 5120, 5) == H + 2374 * 5 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(17408, 5120, 8) == H + 544 * 8 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(8192, 4096, 6) == H + 256 * 6 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(4096, 4096, 8) == H + 256 * 8 * 8
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(5120, 17408, 8) == H + 160 * 8 * 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, 24, 4) == 0
-    # the bound the header states: 4 bytes per row, rows rounded up to 64
+    # the bound the header states: the header plus 4 bytes per row, rows
+    # rounded up to 64
     for R, K in ((1, 16), (16, 32), (65, 512), (4176, 2064), (65620, 528), (151936, 5120)):
         for n in range(1, 9):
-            assert 0 < nv.nvfp4_gemv_argmax_workspace_bytes(R, K, n) <= 4 * (-(-R // 64) * 64), (R, K, n)
+            assert 0 < nv.nvfp4_gemv_argmax_workspace_bytes(R, K, n) <= H + 4 * (-(-R // 64) * 64), (R, K, n)
     assert nv.nvfp4_gemv_argmax_workspace_bytes(16, (1 << 26) + 16, 4) == 0
+
+
+def test_noalloc_array_covers_every_shape_up_to_262144_rows(lib):
+    """The static array of the allocation-free argmax (1 MiB) holds the
+    workspace of every n <= 8 up to 262144 rows: each rows class of the
+    decomposition (small, short-row, 257..512, 513..4096 and more tiles) at
+    its edges and at the limit, for short and long rows."""
+    worst = 0
+    rows = sorted({r for t in (1, 256, 257, 512, 513, 4096, 4097, 16384) for r in (16 * t - 15, 16 * t)} |
+                  {262144 - 63, 262144})
+    for R in rows:
+        for K in (16, 512, 528, 4096, 5120, 17408):
+            for n in range(1, 9):
+                worst = max(worst, nv.nvfp4_gemv_argmax_workspace_bytes(R, K, n))
+    assert 0 < worst <= 1 << 20
+    # the largest row count at n = 8: 16366 four-tile workgroups of 64 rows
+    # fill the array with the header exactly
+    assert nv.nvfp4_gemv_argmax_workspace_bytes(1047424, 16, 8) == 1 << 20
 
 
 @pytest.mark.parametrize("rows,cols,code,scale", [
@@ -276,9 +298,9 @@ def test_binding_rejects_host_and_strided_tensors(lib):
 
 def test_argmax_noalloc_validation(lib):
     g = lib.nvfp4_gemv_argmax_noalloc
-    # the keys of 2^20 rows at n = 8 fill the 1 MiB array; one row more is
-    # rejected before any HIP call
-    assert g(A, B, 1.0, (1 << 20) + 1, 16, C, 8, NULL, A, S0) == EWORKSPACE
+    # the header and the keys of 1047424 rows at n = 8 fill the 1 MiB array;
+    # one row more is rejected before any HIP call
+    assert g(A, B, 1.0, 1047424 + 1, 16, C, 8, NULL, A, S0) == EWORKSPACE
     assert g(A, B, 1.0, 16, 32, C, 9, NULL, A, S0) == EINVAL      # argmax is n <= 8
     assert g(A, B, 1.0, 16, 32, C, 4, NULL, NULL, S0) == EINVAL
     assert g(A, B, 1.0, 16, 32, C, 4, ctypes.c_void_p(0x300002), A, S0) == EALIGN
@@ -305,14 +327,15 @@ def test_batch_workspace_and_validation(lib):
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     wsb = lib.nvfp4_gemv_batch_workspace_bytes
     # the verify pair at n = 4 runs as one launch with the argmax head's four
-    # tiles per workgroup: its 2374 super-tiles give 2374 workgroups x 4 keys
+    # tiles per workgroup: its 2374 super-tiles give 2374 workgroups x 4 keys,
+    # after the head's 1152-byte finish header
     pair = _prods((151936, C, A), (17408, C, NULL))
-    assert wsb(pair, 2, 5120, 4) == 2374 * 4 * 8
+    assert wsb(pair, 2, 5120, 4) == 1152 + 2374 * 4 * 8
     # no argmax: no workspace
     assert wsb(_prods((4096, C, NULL)), 1, 4096, 1) == 0
     # one launch at the larger product's two tiles per workgroup: the
     # 9000-row product's 141 super-tiles give 282 workgroups, not its own 564
-    assert wsb(_prods((70000, C, A), (9000, C, A)), 2, 2048, 1) == (2188 + 282) * 8
+    assert wsb(_prods((70000, C, A), (9000, C, A)), 2, 2048, 1) == 2 * 1152 + (2188 + 282) * 8
     # 8 against 16 waves a row: each product's own decomposition
     mixed = _prods((9000, C, A), (700, C, A))
     assert wsb(mixed, 2, 2048, 3) == (nv.nvfp4_gemv_argmax_workspace_bytes(9000, 2048, 3) +
@@ -324,7 +347,7 @@ def test_batch_workspace_and_validation(lib):
     assert g(pair, 2, 5120, NULL, 4, B, 1 << 20, S0) == EINVAL         # X
     assert g(pair, 2, 5120, MIS, 4, B, 1 << 20, S0) == EALIGN
     assert g(pair, 2, 5128, C, 4, B, 1 << 20, S0) == ESHAPE            # cols % 16
-    assert g(pair, 2, 5120, C, 4, B, 2374 * 4 * 8 - 1, S0) == EWORKSPACE
+    assert g(pair, 2, 5120, C, 4, B, 1152 + 2374 * 4 * 8 - 1, S0) == EWORKSPACE
     assert g(pair, 2, 5120, C, 4, NULL, 1 << 20, S0) == EINVAL         # workspace needed
     assert g(_prods((64, NULL, NULL)), 1, 512, C, 1, NULL, 0, S0) == EINVAL   # neither y nor argmax
     assert g(_prods((64, ctypes.c_void_p(0x300002), NULL)), 1, 512, C, 1, NULL, 0, S0) == EALIGN

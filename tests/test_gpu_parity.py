@@ -280,9 +280,12 @@ def test_matvec_passes_column_identity(fmt, R, K):
     (2000, 1024, 1), (2000, 1024, 4), (2000, 1024, 8),
     # two and four tiles per workgroup past four columns
     (9000, 1040, 6), (65620, 528, 5),
-    # 4219..8438 workgroups: the finish kernel takes two passes over the keys
-    # (per-group loads at n = 1 and 5, the one-column-per-thread loads at 8)
-    (270000, 16, 1), (270000, 16, 5), (270000, 16, 8),
+    # either side of the split finish's thresholds: 12288 keys at one or two
+    # columns, 6144 from three
+    (393216, 16, 1), (393280, 16, 1), (32768, 16, 3), (32832, 16, 3),
+    # one workgroup, 8438 keys in one pass; the split finish (16 workgroups):
+    # one pass over each workgroup's share at 270000 rows, two at 600000
+    (270000, 16, 1), (270000, 16, 5), (270000, 16, 8), (600000, 16, 1), (600000, 16, 8),
 ])
 def test_argmax_matches_oracle(R, K, n):
     wq, ws, c_ref, s_ref = _prepare(R, K, 11 + n + (0 if R == 2000 else R))
@@ -303,7 +306,9 @@ def test_argmax_workspace_reused_across_calls():
     """One workspace of garbage bytes, sized for the largest call, serves
     back-to-back calls of different inputs and shapes."""
     import block_scaled_bit_nvfp4_amd as nv
-    shapes = [(700, 512, 4), (300, 1024, 2), (1300, 512, 8), (700, 512, 4)]
+    # one-workgroup and split finishes in turn: the split one's counter in the
+    # workspace header starts at whatever the last call (or the fill) left
+    shapes = [(700, 512, 4), (270000, 16, 2), (300, 1024, 2), (1300, 512, 8), (270000, 16, 2), (700, 512, 4)]
     size = max(nv.nvfp4_gemv_argmax_workspace_bytes(R, K, n) for R, K, n in shapes)
     wsp = torch.full((size,), 0xFF, dtype=torch.uint8, device=G.DEV)
     for i, (R, K, n) in enumerate(shapes):
@@ -338,6 +343,34 @@ def test_argmax_ties_take_lowest_index():
     z[0, 0] = -0.0
     _, am0 = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, z)
     assert am0.item() == 0
+
+
+def test_argmax_ties_across_split_finish_workgroups():
+    """Equal maxima in the shares of different finish workgroups (270000
+    rows at two columns: 8438 workgroups' keys over the split finish's 16):
+    the lowest row wins, as the oracle's first-maximum rule says."""
+    R, K = 270000, 16
+    rng = np.random.default_rng(17)
+    codes = rng.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales = rng.integers(0x20, 0x40, (R, K // 16), dtype=np.uint8)
+    codes[269999] = 0x77
+    scales[269999] = 0x48
+    for r in (140000, 70001, 7):
+        codes[r], scales[r] = codes[269999], scales[269999]
+    x = torch.ones(2, K, dtype=torch.bfloat16, device=G.DEV)
+    cd, sd = G.canonical_to_dev(codes, scales)
+    wq, ws = G.repack_gpu(cd, sd, R, K)
+    G.note("argmax ties across the split finish")
+    _, am = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, x, with_logits=False)
+    assert list(am.cpu().numpy()) == [7, 7]
+    Y_ref, _ = oracle.gemv(codes, scales, 1.0, G.wl.bf16_bits(x))
+    assert list(oracle.argmax_first(Y_ref)) == [7, 7]
+    # without row 7 the next one, in another finish workgroup's share
+    codes[7] = 0
+    cd, sd = G.canonical_to_dev(codes, scales)
+    wq, ws = G.repack_gpu(cd, sd, R, K)
+    _, am = G.gemv_argmax_gpu(wq, ws, 1.0, R, K, x, with_logits=False)
+    assert list(am.cpu().numpy()) == [70001, 70001]
 
 
 # -------------------------------------------------------------------- SwiGLU

@@ -61,10 +61,11 @@ def test_noalloc_equals_workspace_entry_point_on_two_calls():
 
 
 def test_noalloc_largest_shape_and_the_first_rejected():
-    """2^20 rows at n = 8 use all of the array (one key per 64-row
-    workgroup and column); one row more needs 64 bytes past it and is
-    rejected on the host, before any launch."""
-    R, K, n = 1 << 20, 16, 8
+    """1047424 rows at n = 8 use all of the array (the finish's 1152-byte
+    header, then one key per 64-row workgroup and column); one row more
+    needs a workgroup past it and is rejected on the host, before any
+    launch."""
+    R, K, n = 1047424, 16, 8
     assert nv.nvfp4_gemv_argmax_workspace_bytes(R, K, n) == SCRATCH_BYTES
     assert nv.nvfp4_gemv_argmax_workspace_bytes(R + 1, K, n) > SCRATCH_BYTES
     _, wq, ws = _weights(R, K, 320)
