@@ -329,15 +329,14 @@ argmax_finish_kernel(const unsigned long long *__restrict__ keys, int groups, in
 }
 
 // The split finish: workgroup w reduces its share of the groups to N
-// partial maxima and stores them to the header with device-coherent
-// (agent-scope atomic) stores, which write through the XCD's L2; its first
-// wave waits for their acknowledgement (vmcnt 0, the wait an agent-scope
-// release makes for such stores) and counts the workgroup on the header's
-// counter with an agent-scope add; the workgroup that counts last reads the
-// kFinishGroups x N parts with device-coherent loads and writes the indices.
-// Only the parts cross workgroups and none of them is written through a
-// non-coherent L2 line, so no L2 write-back or invalidate is needed (one per
-// workgroup measured a microsecond slower).  The product zeroed the counter.
+// partial maxima, stores them to the header and counts itself on the
+// header's counter with an agent-scope release add (the barrier before it
+// orders the other threads' part stores before the add); the workgroup that
+// counts last takes an agent-scope acquire fence, reads the kFinishGroups x N
+// parts and writes the indices.  On gfx950 the release is an L2 write-back
+// and the acquire an L2 invalidate (the XCDs' L2s are not coherent); with
+// the L2 holding only the parts, both measured within noise of leaving them
+// out.  The product zeroed the counter.
 constexpr int kSplitFinishThreads = 256;
 
 template <int N>
@@ -372,26 +371,26 @@ argmax_finish_split_kernel(unsigned long long *__restrict__ keys, int groups, in
         if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6][c] = m[c];
     }
     __syncthreads();
-    if (threadIdx.x < kLanes) {   // wave 0: the N part stores, their wait and the count
-        if (threadIdx.x < N) {
-            const int c = threadIdx.x;
-            unsigned long long best = part[0][c];
+    if (threadIdx.x < N) {
+        const int c = threadIdx.x;
+        unsigned long long best = part[0][c];
 #pragma unroll
-            for (int w = 1; w < kSplitFinishThreads / kLanes; ++w) best = part[w][c] > best ? part[w][c] : best;
-            __hip_atomic_store(&parts[int(blockIdx.x) * N + c], best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (threadIdx.x == 0)
-            last = __hip_atomic_fetch_add(finish_counter(keys), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   unsigned(kFinishGroups - 1);
+        for (int w = 1; w < kSplitFinishThreads / kLanes; ++w) best = part[w][c] > best ? part[w][c] : best;
+        parts[int(blockIdx.x) * N + c] = best;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const bool l = __hip_atomic_fetch_add(finish_counter(keys), 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) ==
+                       unsigned(kFinishGroups - 1);
+        if (l) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        last = l;
     }
     __syncthreads();
     if (!last || threadIdx.x >= N) return;
     const int c = threadIdx.x;
     unsigned long long p[kFinishGroups];
 #pragma unroll
-    for (int w = 0; w < kFinishGroups; ++w)
-        p[w] = __hip_atomic_load(&parts[w * N + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int w = 0; w < kFinishGroups; ++w) p[w] = parts[w * N + c];
     unsigned long long best = p[0];
 #pragma unroll
     for (int w = 1; w < kFinishGroups; ++w) best = p[w] > best ? p[w] : best;
