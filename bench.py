@@ -19,7 +19,8 @@ GB/s of algorithmic traffic (compressed weights + activations + outputs);
 `configs` holds each configuration's step time, throughput, layer-tokens/s,
 per-kernel times, its dominant kernel's roofline, the plain-read (or bare
 MFMA) wall measured in the same process at the same byte counts and launch
-counts, and the fp64 CPU oracle timed on a bounded sample of the same
+counts, with, for the matvec configurations, a read-then-store-the-outputs
+wall beside it, and the fp64 CPU oracle timed on a bounded sample of the same
 workload on this host (which also re-checks those GPU outputs).
 """
 from __future__ import annotations
@@ -104,10 +105,12 @@ def gemv_bytes(rows, cols, n, fmt="nvfp4"):
 
 class Launch:
     """One call of the step: the callable, its algorithmic bytes and FLOPs,
-    the kernel it is timed as, and the distinct weight set it reads."""
+    the kernel it is timed as, the distinct weight set it reads, and how many
+    of its bytes are outputs it writes."""
 
-    def __init__(self, fn, nbytes, flops, kernel, weight_key):
+    def __init__(self, fn, nbytes, flops, kernel, weight_key, out_bytes=0):
         self.fn, self.bytes, self.flops, self.kernel, self.weight_key = fn, nbytes, flops, kernel, weight_key
+        self.out_bytes = out_bytes
 
 
 class Step:
@@ -128,7 +131,7 @@ class Step:
             for i, M in enumerate(self.mats):
                 self.launches.append(Launch(self._gemv(M, self.x, 1, self.ys[i % 2]),
                                             gemv_bytes(M.rows, M.cols, 1, w.fmt), 2 * M.rows * M.cols,
-                                            "matvec %dx%d" % (M.rows, M.cols), (M.name, i)))
+                                            "matvec %dx%d" % (M.rows, M.cols), (M.name, i), 4 * M.rows))
         elif name == "mlp_27b_decode":
             gu_m, dn_m = w.matrices
             self.x = wl.activations(1, gu_m.cols, seed=wl.seed_of(name, "x"), device=DEV)
@@ -142,14 +145,15 @@ class Step:
                     # gate||up with SwiGLU in the epilogue (writes h), then down
                     self.launches.append(Launch(self._gemv_swiglu(G_, Dh, F), G_.weight_bytes() + 2 * Dh + 2 * F,
                                                 2 * G_.rows * G_.cols, "gate||up+SwiGLU %dx%d" % (G_.rows, G_.cols),
-                                                ("gate_up", i)))
+                                                ("gate_up", i), 2 * F))
                 else:
                     self.launches.append(Launch(self._gemv(G_, self.x, 1, self.gu), gemv_bytes(G_.rows, G_.cols, 1),
                                                 2 * G_.rows * G_.cols, "gate||up %dx%d" % (G_.rows, G_.cols),
-                                                ("gate_up", i)))
+                                                ("gate_up", i), 4 * G_.rows))
                     self.launches.append(Launch(self._swiglu(F), 2 * F * 4 + F * 2, 4 * F, "SwiGLU", None))
                 self.launches.append(Launch(self._gemv(D, self.h, 1, self.y), gemv_bytes(D.rows, D.cols, 1),
-                                            2 * D.rows * D.cols, "down %dx%d" % (D.rows, D.cols), ("down", i)))
+                                            2 * D.rows * D.cols, "down %dx%d" % (D.rows, D.cols), ("down", i),
+                                            4 * D.rows))
         elif name in ("verify_vocab_n4", "verify_vocab_n8"):
             mw, head = w.matrices
             n = w.n
@@ -170,7 +174,7 @@ class Step:
                                         - n * mw.cols * 2 + 4 * n,
                                         2 * n * (mw.rows + head.rows) * mw.cols,
                                         "matvec+argmax batch %dx%d, %dx%d" % (head.rows, head.cols, mw.rows, mw.cols),
-                                        ("w+lm_head", 0)))
+                                        ("w+lm_head", 0), 4 * n * (mw.rows + head.rows) + 4 * n))
         elif name == "draft_head_8192x4096":
             m = w.matrices[0]
             self.x = wl.activations(1, m.cols, seed=wl.seed_of(name, "x"), device=DEV)
@@ -182,7 +186,7 @@ class Step:
             for i, M in enumerate(self.mats):
                 self.launches.append(Launch(self._argmax(M, self.logits2[i % 2], self.am2[i % 2]),
                                             gemv_bytes(M.rows, M.cols, 1) + 4, 2 * M.rows * M.cols,
-                                            "matvec+argmax %dx%d" % (M.rows, M.cols), (M.name, i)))
+                                            "matvec+argmax %dx%d" % (M.rows, M.cols), (M.name, i), 4 * M.rows + 4))
         elif name in MFMA_WORKLOADS:
             m = w.matrices[0]
             self.x = wl.activations(512, m.cols, seed=wl.seed_of(name, "x"), device=DEV)
@@ -192,7 +196,7 @@ class Step:
             for i, M in enumerate(self.mats):
                 self.launches.append(Launch(self._gemv(M, self.x, 512, self.ys[i % 2]),
                                             gemv_bytes(m.rows, m.cols, 512, w.fmt), 2 * 512 * m.rows * m.cols,
-                                            "wide %dx%d n=512" % (m.rows, m.cols), (M.name, i)))
+                                            "wide %dx%d n=512" % (m.rows, m.cols), (M.name, i), 4 * 512 * m.rows))
         else:
             raise SystemExit("workload %r has no bench step" % name)
         torch.cuda.synchronize()
@@ -326,6 +330,9 @@ class Probe:
         lib.nvfp4_probe_stream_read.restype = ctypes.c_int
         lib.nvfp4_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                                 ctypes.c_void_p]
+        lib.nvfp4_probe_stream_read_store.restype = ctypes.c_int
+        lib.nvfp4_probe_stream_read_store.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                                      ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
         lib.nvfp4_probe_mfma_bf16.restype = ctypes.c_int
         lib.nvfp4_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                               ctypes.c_void_p]
@@ -338,6 +345,13 @@ class Probe:
                                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         if st:
             raise RuntimeError("stream-read probe failed: %s" % nv.nvfp4_strerror(st))
+
+    def read_store(self, buf, rbytes, out, obytes, groups):
+        st = self.lib.nvfp4_probe_stream_read_store(ctypes.c_void_p(buf.data_ptr()), rbytes,
+                                                    ctypes.c_void_p(out.data_ptr()), obytes, groups,
+                                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st:
+            raise RuntimeError("stream-read-store probe failed: %s" % nv.nvfp4_strerror(st))
 
     def mfma(self, groups, waves, iters):
         st = self.lib.nvfp4_probe_mfma_bf16(groups, waves, iters, ctypes.c_void_p(self.sink.data_ptr()),
@@ -353,28 +367,51 @@ def read_wall(probe, step, steps, warmup, per_graph):
     """The plain-read wall of a step: one streaming read per product launch,
     of that launch's algorithmic bytes, each distinct weight set with its own
     buffer (so the working set matches), in step order in one HIP graph.
-    The read's grid is swept per launch size and the fastest kept."""
+    The read's grid is swept per launch size and the fastest kept.  Beside
+    it, the read-and-store wall: each launch reads its input bytes and then
+    writes its output bytes (rounded up to 16) from every workgroup after
+    its reads, as a product writes its outputs after its sums."""
     reads = [L for L in step.launches if L.weight_key is not None]
     bufs = {}
     for L in reads:
         if L.weight_key not in bufs:
             bufs[L.weight_key] = torch.empty(L.bytes, dtype=torch.uint8, device=DEV).fill_(0x5A)
-    best = {}
-    for size in sorted({L.bytes for L in reads}):
-        same = [L for L in reads if L.bytes == size]
-        t = {}
-        for g in READ_GROUPS:
-            _, t[g] = time_graph(lambda: [probe.read(bufs[L.weight_key], L.bytes, g) for L in same], 10, 2)
-        best[size] = min(t, key=t.get)
-    _, ev = time_graph(lambda: [probe.read(bufs[L.weight_key], L.bytes, best[L.bytes]) for L in reads],
+    obytes = {id(L): (L.out_bytes + 15) // 16 * 16 for L in reads}
+    outs = [torch.empty(max(16, max(obytes.values())), dtype=torch.uint8, device=DEV) for _ in range(2)]
+
+    def sweep(one):
+        best = {}
+        for size in sorted({L.bytes for L in reads}):
+            same = [L for L in reads if L.bytes == size]
+            t = {}
+            for g in READ_GROUPS:
+                _, t[g] = time_graph(lambda: [one(L, i, g) for i, L in enumerate(same)], 10, 2)
+            best[size] = min(t, key=t.get)
+        return best
+
+    def plain(L, i, g):
+        probe.read(bufs[L.weight_key], L.bytes, g)
+
+    def with_store(L, i, g):
+        probe.read_store(bufs[L.weight_key], L.bytes - L.out_bytes, outs[i % 2], obytes[id(L)], g)
+
+    best = sweep(plain)
+    _, ev = time_graph(lambda: [plain(L, i, best[L.bytes]) for i, L in enumerate(reads)],
                        steps, warmup, per_graph)
+    best_s = sweep(with_store)
+    _, ev_s = time_graph(lambda: [with_store(L, i, best_s[L.bytes]) for i, L in enumerate(reads)],
+                         steps, warmup, per_graph)
     nbytes = sum(L.bytes for L in reads)
-    del bufs
+    del bufs, outs
     return {"kind": "plain read", "us_per_step": round(ev * 1e6, 3), "gbs": round(nbytes / ev / 1e9, 1),
             "launches_per_step": len(reads), "bytes_per_step": nbytes, "steps_per_replay": per_graph,
             "groups": {str(s): g for s, g in best.items()},
             "how": "one nontemporal 128-bit streaming read per product launch, of that launch's algorithmic "
-                   "bytes, the grid (256-thread workgroups) swept per size, in one HIP graph"}
+                   "bytes, the grid (256-thread workgroups) swept per size, in one HIP graph",
+            "read_store": {"us_per_step": round(ev_s * 1e6, 3), "gbs": round(nbytes / ev_s / 1e9, 1),
+                           "groups": {str(s): g for s, g in best_s.items()},
+                           "how": "the same launches reading their input bytes, then each workgroup storing "
+                                  "its share of the launch's output bytes with 128-bit stores after its reads"}}
 
 
 def mfma_wall(probe):
@@ -594,6 +631,7 @@ def measure(name, args, probe, mfma_peak=None):
         e["measured_wall"] = wall
         # the same bytes: the wall's time over the step's
         e["pct_of_measured_wall"] = round(100 * wall["us_per_step"] / (step_s * 1e6), 2)
+        e["pct_of_read_store_wall"] = round(100 * wall["read_store"]["us_per_step"] / (step_s * 1e6), 2)
     if name == "mlp_27b_decode":
         e["mlp"] = ("three launches per layer" if args.mlp_three_launches else
                     "two launches per layer (gate||up with SwiGLU fused, down)")
@@ -674,8 +712,9 @@ def main():
         "roofline": e["roofline"],
     }
     result["config"]["timing"] = "HIP graph replays, %d step(s) per replay" % e["steps_per_replay"]
-    if "pct_of_measured_wall" in e:
-        result["config"]["pct_of_measured_wall"] = e["pct_of_measured_wall"]
+    for k in ("pct_of_measured_wall", "pct_of_read_store_wall"):
+        if k in e:
+            result["config"][k] = e[k]
     if "cpu_baseline" in e:
         result["cpu_baseline"] = e["cpu_baseline"]
     result["host"] = host_facts()

@@ -44,6 +44,31 @@ __global__ void __launch_bounds__(kThreads) stream_read_kernel(const uint8_t *bu
     if (a == kMagic) sink[0] = a;
 }
 
+// The same read of `rbytes` bytes, then workgroup g stores its share
+// [g * oshare, (g + 1) * oshare) of the `obytes`-byte output (oshare a
+// multiple of 16) with 128-bit stores whose value comes from its loads, so
+// they wait for them, as a product's outputs wait for its sums.
+__global__ void __launch_bounds__(kThreads) stream_read_store_kernel(const uint8_t *buf, uint64_t rbytes, uint32_t rshare,
+                                                                     uint8_t *out, uint64_t obytes, uint32_t oshare) {
+    const uint64_t start = uint64_t(blockIdx.x) * rshare;
+    const uint32_t mine = start >= rbytes ? 0u : uint32_t(rbytes - start < rshare ? rbytes - start : rshare);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(buf + (start < rbytes ? start : 0)),
+                                                      (short)0, int(mine), 0x00020000);
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (uint32_t off = threadIdx.x * 16u; off < mine; off += kRound * kUnroll) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + u * kRound, 0, 2));
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+    }
+    const uint64_t ostart = uint64_t(blockIdx.x) * oshare;
+    const uint32_t omine = ostart >= obytes ? 0u : uint32_t(obytes - ostart < oshare ? obytes - ostart : oshare);
+    for (uint32_t off = threadIdx.x * 16u; off + 16u <= omine; off += kRound)
+        *reinterpret_cast<u32x4 *>(out + ostart + off) = acc;
+}
+
 __global__ void __launch_bounds__(1024) mfma_probe_kernel(int iters, float *sink) {
     const int lane = threadIdx.x & 63;
     bf16x8 a, b;
@@ -77,6 +102,23 @@ PROBE_API int nvfp4_probe_stream_read(const void *buf, size_t bytes, int groups,
     (void)hipGetLastError();
     hipLaunchKernelGGL(stream_read_kernel, dim3(unsigned(groups)), dim3(kThreads), 0, stream,
                        static_cast<const uint8_t *>(buf), uint64_t(bytes), uint32_t(share), sink);
+    return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
+}
+
+PROBE_API int nvfp4_probe_stream_read_store(const void *buf, size_t rbytes, void *out, size_t obytes, int groups,
+                                            hipStream_t stream) {
+    if (!buf || !out || groups < 1 || groups > 65536) return NVFP4_EINVAL;
+    if (rbytes < 16 || rbytes >= (size_t(1) << 31) || obytes < 16 || obytes >= (size_t(1) << 31) || obytes % 16)
+        return NVFP4_ESHAPE;
+    if (reinterpret_cast<uintptr_t>(buf) % 16 || reinterpret_cast<uintptr_t>(out) % 16) return NVFP4_EALIGN;
+    const size_t per = (rbytes + size_t(groups) - 1) / size_t(groups);
+    const size_t rshare = (per + kRound - 1) / kRound * kRound;
+    const size_t oper = (obytes + size_t(groups) - 1) / size_t(groups);
+    const size_t oshare = (oper + 15) / 16 * 16;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(stream_read_store_kernel, dim3(unsigned(groups)), dim3(kThreads), 0, stream,
+                       static_cast<const uint8_t *>(buf), uint64_t(rbytes), uint32_t(rshare), static_cast<uint8_t *>(out),
+                       uint64_t(obytes), uint32_t(oshare));
     return hipGetLastError() == hipSuccess ? NVFP4_OK : NVFP4_EHIP;
 }
 

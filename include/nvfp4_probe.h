@@ -2,7 +2,7 @@
  * nvfp4_probe.h -- C ABI of libnvfp4_probe: the measured walls the NVFP4
  * products are reported against.  A measurement aid, not part of the
  * product: the bw24 README (performance notes) reports its best kernel as a
- * fraction of a measured DRAM wall beside the nominal peak, and these two
+ * fraction of a measured DRAM wall beside the nominal peak, and these
  * kernels measure that wall on this GPU in the same process as the
  * products, at their byte counts and launch counts.
  *
@@ -27,6 +27,15 @@ extern "C" {
  * thread, and fold them with XOR; nothing is stored unless the fold hits a
  * fixed 32-bit value (then one word to sink[0]).  1 <= groups <= 65536. */
 int nvfp4_probe_stream_read(const void *buf, size_t bytes, int groups, uint32_t *sink, hipStream_t stream);
+
+/* The same read of `rbytes` bytes at `buf`, then each workgroup stores its
+ * contiguous share of the `obytes`-byte output at `out` (16-byte aligned,
+ * obytes a multiple of 16, both sizes < 2^31) with 128-bit stores whose
+ * values come from its loads, as a product stores its outputs after its
+ * sums: the wall of a launch that reads a product's inputs and writes its
+ * outputs.  1 <= groups <= 65536. */
+int nvfp4_probe_stream_read_store(const void *buf, size_t rbytes, void *out, size_t obytes, int groups,
+                                  hipStream_t stream);
 
 /* A bare loop of v_mfma_f32_16x16x32_bf16: `groups` workgroups of
  * `waves` waves (1..16), each wave `iters` rounds of eight independent

@@ -367,3 +367,36 @@ def test_binding_batch_checks_every_product(lib):
         nv.nvfp4_gemv_batch([dict(ok, y=torch.zeros(n, R - 1))], K, X, n)
     with pytest.raises(ValueError, match="must be in GPU memory"):
         nv.nvfp4_gemv_batch([ok], K, X, n)
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "nvfp4_probe.h")
+
+
+def test_probe_library_exports_its_header_and_checks_arguments():
+    """libnvfp4_probe (the measured walls) exports every function
+    include/nvfp4_probe.h declares; the read-and-store probe rejects bad
+    arguments on the host (no call here passes validation, so none launches)."""
+    path = os.path.join(ROOT, "block_scaled_bit_nvfp4_amd", "libnvfp4_probe.so")
+    if not os.path.exists(path):
+        from block_scaled_bit_nvfp4_amd import build
+        build.build(verbose=False)
+    plib = ctypes.CDLL(path)
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(nvfp4_probe_\w+)\s*\(", text)))
+    assert "nvfp4_probe_stream_read_store" in names
+    for name in names:
+        assert hasattr(plib, name), name
+    f = plib.nvfp4_probe_stream_read_store
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    buf, out, mis = ctypes.c_void_p(0x200000), ctypes.c_void_p(0x400000), ctypes.c_void_p(0x200004)
+    assert f(None, 4096, out, 4096, 8, None) == EINVAL
+    assert f(buf, 4096, None, 4096, 8, None) == EINVAL
+    assert f(buf, 4096, out, 4096, 0, None) == EINVAL             # groups
+    assert f(buf, 4096, out, 4096, 65537, None) == EINVAL
+    assert f(buf, 8, out, 4096, 8, None) == ESHAPE                # read size
+    assert f(buf, 1 << 31, out, 4096, 8, None) == ESHAPE
+    assert f(buf, 4096, out, 4100, 8, None) == ESHAPE             # output not a multiple of 16
+    assert f(buf, 4096, out, 0, 8, None) == ESHAPE
+    assert f(mis, 4096, out, 4096, 8, None) == EALIGN
+    assert f(buf, 4096, mis, 4096, 8, None) == EALIGN
