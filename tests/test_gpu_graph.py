@@ -71,6 +71,27 @@ def _calls():
              dict(wq=a[0], ws=a[1], tscale=0.7, rows=2000, y=yb)]
     bw = torch.empty(max(8, nv.nvfp4_gemv_batch_workspace_bytes(prods, K, 4)), dtype=torch.uint8, device=G.DEV)
     out.append(("nvfp4_gemv_batch n=4", lambda: nv.nvfp4_gemv_batch(prods, K, X[4], 4, bw), [yb, lb, ab]))
+    # the split argmax finish (more than 12288 keys at two columns, 6144 from
+    # three): its counter in the workspace header is zeroed by the product
+    # on every replay
+    K2 = 16
+    X2 = {n: G.seeded_x(n, K2, seed=310 + n) for n in (2, 8)}
+    e = _nv(270000, K2, 307)
+    for n in (2, 8):
+        am_s = i32(n)
+        ws_s = torch.empty(nv.nvfp4_gemv_argmax_workspace_bytes(270000, K2, n), dtype=torch.uint8, device=G.DEV)
+        out.append(("nvfp4_gemv_argmax split finish n=%d" % n,
+                    lambda n=n, am_s=am_s, ws_s=ws_s: nv.nvfp4_gemv_argmax(e[0], e[1], 1.0, 270000, K2, X2[n], n, None,
+                                                                           am_s, ws_s), [am_s]))
+    am_n = i32(8)
+    out.append(("nvfp4_gemv_argmax_noalloc split finish n=8",
+                lambda: nv.nvfp4_gemv_argmax_noalloc(e[0], e[1], 1.0, 270000, K2, X2[8], 8, None, am_n), [am_n]))
+    f2 = _nv(4000, K2, 308)
+    y2, a2 = f32(2, 4000), i32(2)
+    prods2 = [dict(wq=e[0], ws=e[1], tscale=1.0, rows=270000, argmax=a2),
+              dict(wq=f2[0], ws=f2[1], tscale=1.0, rows=4000, y=y2)]
+    bw2 = torch.empty(nv.nvfp4_gemv_batch_workspace_bytes(prods2, K2, 2), dtype=torch.uint8, device=G.DEV)
+    out.append(("nvfp4_gemv_batch split finish n=2", lambda: nv.nvfp4_gemv_batch(prods2, K2, X2[2], 2, bw2), [y2, a2]))
     return out
 
 
