@@ -441,21 +441,26 @@ int launch_narrow(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float
 
 int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
                 int n, float *Y, hipStream_t stream, int fmt = kNvfp4);
-bool wide_fills_device(const Geometry &g, int n, int fmt);
+double wide_estimate_us(const Geometry &g, int n, int fmt);
 
-// Products of 9..32 columns as passes of the matvec over column chunks of
-// at most eight (columns [8p, 8p + 8) of X and Y in pass p): each column then
-// has the bits of its one-column product, and the weights are read once per
-// pass.  The wide product costs the same from 9 to 128 columns (its
-// workgroups each decode their weights for a 128-column tile), so two passes
-// always beat it; three or four only where its workgroups do not fill the
-// CUs or cannot take the shape (17408 x 5120: 29 us for 16 columns in two
-// passes against 65 us).  Returns the number of passes, 0 for the wide
-// product.
+// Products of 9..128 columns either as passes of the matvec over column
+// chunks of at most eight (columns [8p, 8p + 8) of X and Y in pass p: each
+// column then has the bits of its one-column product, and the weights are
+// read once per pass), or as the wide product, whichever is estimated
+// faster.  A pass costs about the read of the weights at 4 TB/s plus 2.5 us
+// (17408 x 5120: 12.5-13.8 us, 4096 x 4096: 4.3-4.6 us, 5120 x 17408: 15 us
+// measured); the wide product's estimate follows its shape and workgroup
+// rounds (wide_estimate_us).  So 17408 x 5120 takes two passes up to 16
+// columns (28 against 30 us) and the wide product from 17 (30.5 us at 32
+// columns against 53 us in four passes), while 4096 x 4096 and 5120 x 17408
+// keep passes to about 48 and 56 columns.  Returns the number of passes, 0
+// for the wide product.
 int narrow_passes(const Geometry &g, int n, int fmt) {
-    if (n <= kMaxNarrowN || n > 4 * kMaxNarrowN || g.cols > kMaxNarrowCols) return 0;
+    if (n <= kMaxNarrowN || n > 16 * kMaxNarrowN || g.cols > kMaxNarrowCols) return 0;
     const int passes = int(ceil_div(n, kMaxNarrowN));
-    return passes <= 2 || !wide_fills_device(g, n, fmt) ? passes : 0;
+    const double pass_us = double(g.code_bytes() + g.scale_bytes(fmt)) / 4.0e6 + 2.5;
+    const double wide_us = wide_estimate_us(g, n, fmt);
+    return wide_us < 0.0 || double(passes) * pass_us <= wide_us ? passes : 0;
 }
 
 template <typename Launch>

@@ -52,30 +52,53 @@
 
 namespace nvfp4 {
 
-constexpr int kWideSupers = 4;                  // super-tiles per workgroup
-constexpr int kWaveTiles = 2;                   // tiles per wave
-constexpr int kWideWaves = kWideSupers * kSuperTiles / kWaveTiles;   // 8
-constexpr int kWideCols = 128;                  // activation columns per workgroup
-constexpr int kWideSub = kWideCols / 16;        // column subtiles of an MFMA (one per wave for the extra tile)
+constexpr int kWideWaves = 8;                   // waves per workgroup
 constexpr int kXColBytes = kOctet * kBlock * 2; // one column's octet: 128 bf16
-constexpr int kXBuf = kWideCols * kXColBytes;   // one octet of the X tile: 32 KiB
 constexpr int kXRing = 2;                       // octets of X in LDS
-constexpr int kXDmaPerWave = kXBuf / (kWideWaves * kLanes * 16);   // 16-byte lanes
-// One octet of the workgroup's weights in LDS: per wave its two code chunks
-// and its tiles' scale bytes as two dword planes; then, for each of the
-// waves that decode the extra tile (one 32-k slice each), its own copy of
-// the extra tile's code chunk and scale bytes.
-constexpr int kWWave = kWaveTiles * kCodeChunk + 2 * 256;   // 2.5 KiB
 constexpr int kXDecoders = 4;                   // waves decoding the extra tile, one slice each
 constexpr int kWXWave = kCodeChunk + 256;       // a decoder's raw extra tile: code, then 128 scale bytes
-constexpr int kWXCode = kWideWaves * kWWave;
-constexpr int kWStage = kWXCode + kXDecoders * kWXWave;
 constexpr int kWRing = 3;                       // octets of weights in LDS
 // The extra tile's decoded A operands of one octet: 4 slices x 64 lanes x
 // 16 bytes, in a ring of two octets.
 constexpr int kXABuf = 4 * kLanes * 16;
 constexpr int kXARing = 2;
-constexpr int kWideLds = kXRing * kXBuf + kWRing * kWStage + kXARing * kXABuf;
+
+// The shape of a workgroup: eight waves, each taking WT tiles of the
+// workgroup's SUP super-tiles over its CS 16-column subtiles of X.  The
+// product shape (two tiles per wave, four super-tiles, 128 columns) is the
+// one described above, with its extra tiles.  The narrower shapes (one tile
+// per wave, two super-tiles: twice the workgroups for the same rows) take
+// 128, 64 or 32 columns for products of 9 to 128 columns, where the product
+// shape's workgroups would leave CUs idle and its 128-column tile would
+// spend LDS reads and MFMAs on columns past n.  One weight decode feeds CS
+// MFMAs in every shape; each output is the same MFMA chain over the same k
+// order in every shape, so the shape changes no result bit.
+template <int WT, int SUP, int CS>
+struct WideShape {
+    static constexpr int kWaveTiles = WT;
+    static constexpr int kSupers = SUP;
+    static constexpr int kSub = CS;                        // column subtiles per wave
+    static constexpr int kCols = 16 * CS;                  // activation columns per workgroup
+    static constexpr int kXBuf = kCols * kXColBytes;       // one octet of the X tile
+    static constexpr int kXDmaPerWave = kXBuf / (kWideWaves * kLanes * 16);   // 16-byte lanes
+    static constexpr bool kExtra = WT == 2 && SUP == 4 && CS == 8;             // the extra-tile balancing
+    // One octet of the workgroup's weights in LDS: per wave its code chunks
+    // and its tiles' scale bytes as two dword planes; then, with the extra
+    // tile, for each of the waves that decode it (one 32-k slice each), its
+    // own copy of the extra tile's code chunk and scale bytes.
+    static constexpr int kWWave = WT * kCodeChunk + 2 * 256;
+    static constexpr int kWXCode = kWideWaves * kWWave;
+    static constexpr int kWStage = kWXCode + (kExtra ? kXDecoders * kWXWave : 0);
+    static constexpr int kLds = kXRing * kXBuf + kWRing * kWStage + (kExtra ? kXARing * kXABuf : 0);
+    static_assert(SUP * kSuperTiles / WT == kWideWaves, "eight waves per workgroup");
+    static_assert(kXDmaPerWave >= 1 && kXDmaPerWave * kWideWaves * kLanes * 16 == kXBuf, "whole X staging rounds");
+    static_assert(CS % WT == 0, "a wave's decodes fall between its column subtiles");
+};
+using ShapeProduct = WideShape<2, 4, 8>;   // wide products; 148 KiB of LDS
+using ShapeMid128 = WideShape<1, 2, 8>;
+using ShapeMid64 = WideShape<1, 2, 4>;
+using ShapeMid32 = WideShape<1, 2, 2>;
+enum WideShapeId { kShapeProduct = 0, kShapeMid128 = 1, kShapeMid64 = 2, kShapeMid32 = 3 };
 constexpr int kXcds = 8;
 // Longest rows of the wide product: a column tile of X and a super-tile's
 // code stream stay below 2^31 bytes of buffer offset.
@@ -117,22 +140,26 @@ __device__ __forceinline__ uint32_t xtile_offset(int c, int j) {
 
 // Host-chosen decomposition (a function of rows, cols, n and the CU count).
 struct WideConfig {
-    int col_groups;   // 128-column tiles of X
-    int row_groups;   // workgroups per column tile, four super-tiles each
-    int extra;        // workgroups (per column tile) that also take one remaining tile
+    int shape;        // WideShapeId
+    int col_groups;   // column tiles of X
+    int row_groups;   // workgroups per column tile
+    int extra;        // workgroups (per column tile) that also take one remaining tile (product shape)
     int64_t groups;   // launched workgroups (whole XCD rounds; the excess leaves at once)
 };
 
 // FMT kMxfp4: the scale plane holds a row's four E8M0 bytes per octet, and
 // word d of a code entry (32-element block d of the octet) is decoded by the
 // scaled conversion alone (the power of two goes into its scale operand).
-template <int FMT>
+template <int FMT, class S>
 __device__ __forceinline__ void
 wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows, int supertiles,
           int octets, int K, const uint16_t *__restrict__ X, int n, float *__restrict__ Y, int row_groups,
           int col_groups, int extra, int vec_store) {
     extern __shared__ __attribute__((aligned(16))) uint8_t xs[];   // X ring, then the weight ring
     asm volatile("" ::: "a0");   // lets the accumulators live in AGPRs
+    constexpr int kWaveTiles = S::kWaveTiles, kWideSupers = S::kSupers, kWideCols = S::kCols, kWideSub = S::kSub;
+    constexpr int kXBuf = S::kXBuf, kXDmaPerWave = S::kXDmaPerWave;
+    constexpr int kWWave = S::kWWave, kWXCode = S::kWXCode, kWStage = S::kWStage;
 
     // Workgroup -> (row group, column tile): the column tiles of a row group
     // are consecutive workgroups of one XCD.
@@ -147,10 +174,12 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
     const int n0 = cg * kWideCols;
     const int c16 = lane & 15, g = lane >> 4;
 
-    // This wave's tiles: 2 half, 2 half + 1 of super-tile unit; a super-tile
-    // past the last reads zeros and stores nothing.
-    const int unit = rg * kWideSupers + (wave >> 1);
-    const int half = wave & 1;
+    // This wave's tiles: kWaveTiles half .. kWaveTiles (half + 1) - 1 of
+    // super-tile unit; a super-tile past the last reads zeros and stores
+    // nothing.
+    constexpr int kWavesPerSuper = kSuperTiles / kWaveTiles;
+    const int unit = rg * kWideSupers + wave / kWavesPerSuper;
+    const int half = wave % kWavesPerSuper;
     const bool has_unit = unit < supertiles;
     constexpr int SREGION = FMT == kMxfp4 ? kMxScaleRegion : kScaleRegion;
     constexpr int SCHUNK = FMT == kMxfp4 ? kMxScaleChunk : kScaleChunk;
@@ -161,7 +190,7 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
                                has_unit ? uint32_t(octets) * SREGION : 0u);
     // The extra tile of this workgroup (each wave takes column subtile wave).
     const int xtile = row_groups * kWideSupers * kSuperTiles + rg;
-    const bool has_extra = rg < extra && xtile < supertiles * kSuperTiles;
+    const bool has_extra = S::kExtra && rg < extra && xtile < supertiles * kSuperTiles;
     const int64_t xbase = has_extra ? int64_t(xtile >> 2) * octets : 0;
     const auto xcrs = make_rsrc(wq + xbase * kCodeRegion + (xtile & 3) * kCodeChunk,
                                 has_extra ? uint32_t(octets) * kCodeRegion : 0u);
@@ -206,15 +235,15 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
                                                          0, 0, kStream);
         } else if (part == 1) {
         if constexpr (FMT == kMxfp4) {
-            const uint32_t so = lane < 32 ? uint32_t(o) * SREGION + uint32_t(lane) * 4u : kOutOfRange;
+            const uint32_t so = lane < 16 * kWaveTiles ? uint32_t(o) * SREGION + uint32_t(lane) * 4u : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk), 4, so, 0, 0, kStream);
         } else {
-            const uint32_t so = lane < 32 ? uint32_t(o) * SREGION + uint32_t(lane) * 8u : kOutOfRange;
+            const uint32_t so = lane < 16 * kWaveTiles ? uint32_t(o) * SREGION + uint32_t(lane) * 8u : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk), 4, so, 0, 0, kStream);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, lds_ptr(mine + kWaveTiles * kCodeChunk + 256), 4,
                                                      so == kOutOfRange ? so : so + 4, 0, 0, kStream);
         }
-        } else if (wave < kXDecoders) {
+        } else if (S::kExtra && wave < kXDecoders) {
             uint8_t *xw = dst + kWXCode + wave * kWXWave;
             // the extra tile's 16 rows of scale bytes: 8 per row (NVFP4) or 4 (MXFP4)
             const int xlanes = FMT == kMxfp4 ? 16 : 32;
@@ -233,8 +262,8 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
     // issue order; the waits below leave exactly the newest load_w
     // outstanding, so everything issued before it has landed in LDS.)
     constexpr int kWLoadsOwn = kWaveTiles + (FMT == kMxfp4 ? 1 : 2);
-    constexpr int kWLoadsDec = kWLoadsOwn + 2;
-    const bool xdecoder = wave < kXDecoders;   // issues the extra tile's loads (zeros when there is none)
+    constexpr int kWLoadsDec = kWLoadsOwn + (S::kExtra ? 2 : 0);
+    const bool xdecoder = S::kExtra && wave < kXDecoders;   // issues the extra tile's loads (zeros when there is none)
     // A decoder wave turns slice d = wave of the extra tile's octet o into
     // exact bf16 A operands for every lane, from its own copy of the raw
     // bytes, into the extra ring (published by the next barrier).
@@ -341,7 +370,8 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
                 for (int tt = 0; tt < kWaveTiles; ++tt)
                     acc[tt][cs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[cur][tt], bv[cs], acc[tt][cs], 0, 0, 0);
                 if (d < 3) bv[cs] = read_b(d + 1, cs);
-                if (d < 3 && (cs & 3) == 3) a[nxt][cs >> 2] = decode(d + 1, cs >> 2);
+                constexpr int kPer = kWideSub / kWaveTiles;   // subtiles between a wave's decodes
+                if (d < 3 && cs % kPer == kPer - 1) a[nxt][cs / kPer] = decode(d + 1, cs / kPer);
             }
             if (EXTRA) {
                 xacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[cur], xbv, xacc, 0, 0, 0);
@@ -396,8 +426,12 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
             compute(o, extra_c, o + 2 < octets ? o + 2 : -1);
         }
     };
-    if (has_extra) run(std::true_type{});
-    else run(std::false_type{});
+    if constexpr (S::kExtra) {
+        if (has_extra) run(std::true_type{});
+        else run(std::false_type{});
+    } else {
+        run(std::false_type{});
+    }
 
     // Lane (g, c16) holds rows 4g .. 4g + 3 of a tile for column
     // cs * 16 + c16 of the column tile.
@@ -423,21 +457,41 @@ wide_body(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float 
     if (has_extra) store(xacc, xtile * kTileRows + 4 * g, n0 + wave * 16 + c16);
 }
 
-// The decomposition: workgroups of four super-tiles per 128-column tile.
-// When those workgroups would overshoot a whole number of CU rounds by at
-// most one tile per workgroup, the row groups are cut back to the whole
-// rounds and the remaining tiles become the workgroups' extra tiles.
+// Super-tiles per workgroup and columns per workgroup of each shape.
+constexpr int kShapeSupers[4] = {ShapeProduct::kSupers, ShapeMid128::kSupers, ShapeMid64::kSupers, ShapeMid32::kSupers};
+constexpr int kShapeCols[4] = {ShapeProduct::kCols, ShapeMid128::kCols, ShapeMid64::kCols, ShapeMid32::kCols};
+
+// The shape for n columns: up to 32 and 64 columns the 32- and 64-column
+// shapes (faster than the product shape on every matrix measured: 34816 x
+// 5120 at 48 columns 55 against 72 us, the 151936 x 5120 head 147 against
+// 226 us); up to 128 the 128-column narrow shape while its workgroups (two
+// super-tiles each, one per CU for their 100 KiB of LDS) fit one round of
+// the CUs, else the product shape (34816 x 5120 at 128 columns: two rounds
+// of the narrow shape 98.9 us, one of the product shape 79.5 us).
+inline int wide_shape(const Geometry &g, int n, int cus) {
+    if (n > 128) return kShapeProduct;
+    if (n > 64) return ceil_div(g.supertiles, int64_t(kShapeSupers[kShapeMid128])) <= cus ? kShapeMid128 : kShapeProduct;
+    return n > 32 ? kShapeMid64 : kShapeMid32;
+}
+
+// The decomposition: workgroups of the shape's super-tiles per column tile.
+// For the product shape, when those workgroups would overshoot a whole
+// number of CU rounds by at most one tile per workgroup, the row groups are
+// cut back to the whole rounds and the remaining tiles become the
+// workgroups' extra tiles.
 inline WideConfig wide_config(const Geometry &g, int n, int cus) {
     WideConfig c;
-    c.col_groups = int(ceil_div(n, kWideCols));
-    c.row_groups = int(ceil_div(g.supertiles, kWideSupers));
+    c.shape = wide_shape(g, n, cus);
+    const int supers = kShapeSupers[c.shape];
+    c.col_groups = int(ceil_div(n, kShapeCols[c.shape]));
+    c.row_groups = int(ceil_div(g.supertiles, int64_t(supers)));
     c.extra = 0;
-    if (cus > 0 && cus % c.col_groups == 0) {
+    if (c.shape == kShapeProduct && cus > 0 && cus % c.col_groups == 0) {
         const int64_t per_round = cus / c.col_groups;                  // row groups per CU round
-        const int64_t rounds = (g.supertiles / kWideSupers) / per_round;
+        const int64_t rounds = (g.supertiles / supers) / per_round;
         if (rounds >= 1) {
             const int64_t rg = rounds * per_round;
-            const int64_t left_tiles = (g.supertiles - rg * kWideSupers) * kSuperTiles;
+            const int64_t left_tiles = (g.supertiles - rg * supers) * kSuperTiles;
             if (left_tiles > 0 && left_tiles <= rg) {
                 c.row_groups = int(rg);
                 c.extra = int(left_tiles);
@@ -448,26 +502,28 @@ inline WideConfig wide_config(const Geometry &g, int n, int cus) {
     return c;
 }
 
-// The two formats' kernels.
+// The two formats' kernels, one per shape.
+template <class S>
 __global__ void __launch_bounds__(kWideWaves * kLanes, 2)
 wide_kernel_nvfp4(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows,
                   int supertiles, int octets, int K, const uint16_t *__restrict__ X, int n, float *__restrict__ Y,
                   int row_groups, int col_groups, int extra, int vec_store) {
-    wide_body<kNvfp4>(wq, ws, tscale, rows, supertiles, octets, K, X, n, Y, row_groups, col_groups, extra, vec_store);
+    wide_body<kNvfp4, S>(wq, ws, tscale, rows, supertiles, octets, K, X, n, Y, row_groups, col_groups, extra, vec_store);
 }
 
+template <class S>
 __global__ void __launch_bounds__(kWideWaves * kLanes, 2)
 wide_kernel_mxfp4(const uint8_t *__restrict__ wq, const uint8_t *__restrict__ ws, float tscale, int rows,
                   int supertiles, int octets, int K, const uint16_t *__restrict__ X, int n, float *__restrict__ Y,
                   int row_groups, int col_groups, int extra, int vec_store) {
-    wide_body<kMxfp4>(wq, ws, tscale, rows, supertiles, octets, K, X, n, Y, row_groups, col_groups, extra, vec_store);
+    wide_body<kMxfp4, S>(wq, ws, tscale, rows, supertiles, octets, K, X, n, Y, row_groups, col_groups, extra, vec_store);
 }
 
 // Per-device facts the wide launch needs, taken once per device on its first
 // wide call (with that device current): the CU count, which the
-// decomposition follows, and the dynamic-LDS attribute of both wide kernels,
-// whose rings (148 KiB) are above the default limit.  Later calls only look
-// up the current device's index.
+// decomposition follows, and the dynamic-LDS attribute of every wide kernel
+// whose rings are above the default limit (the product shape's 148 KiB).
+// Later calls only look up the current device's index.
 constexpr int kMaxDevices = 64;
 struct WideDevice {
     std::once_flag once;
@@ -476,27 +532,56 @@ struct WideDevice {
 };
 static WideDevice g_wide_devices[kMaxDevices];
 
+template <class S>
+static bool set_wide_lds() {
+    if (S::kLds <= 65536) return true;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(wide_kernel_nvfp4<S>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, S::kLds) == hipSuccess &&
+           hipFuncSetAttribute(reinterpret_cast<const void *>(wide_kernel_mxfp4<S>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, S::kLds) == hipSuccess;
+}
+
 static const WideDevice *wide_device() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
     WideDevice &w = g_wide_devices[dev];
     std::call_once(w.once, [&w, dev] {
         if (hipDeviceGetAttribute(&w.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) w.cus = 0;
-        w.lds_ok = hipFuncSetAttribute(reinterpret_cast<const void *>(wide_kernel_nvfp4),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds) == hipSuccess &&
-                   hipFuncSetAttribute(reinterpret_cast<const void *>(wide_kernel_mxfp4),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kWideLds) == hipSuccess;
+        w.lds_ok = set_wide_lds<ShapeProduct>() && set_wide_lds<ShapeMid128>() && set_wide_lds<ShapeMid64>() &&
+                   set_wide_lds<ShapeMid32>();
     });
     return &w;
 }
 
-// True when the wide product takes the shape and its workgroups at n
-// columns are at least the device's CUs (false where the device cannot be
-// queried).
-bool wide_fills_device(const Geometry &g, int n, int fmt) {
-    if (g.cols > kMaxWideCols || int64_t(g.scale_bytes(fmt)) > kMaxWideScaleBytes) return false;
+// Estimated duration in microseconds of the wide product at n columns on
+// this device, or a negative value when it cannot take the shape (or the
+// device cannot be queried).  A workgroup of each shape spends about this
+// long per octet of its rows, measured on 17408 x 5120, 4096 x 4096 and
+// 5120 x 17408 with one round of workgroups: 1.6 us (product shape), 1.2
+// (128-column narrow shape), 0.85 (64 columns) and 0.75 (32 columns); a
+// launch adds about 2 us.
+double wide_estimate_us(const Geometry &g, int n, int fmt) {
+    if (g.cols > kMaxWideCols || int64_t(g.scale_bytes(fmt)) > kMaxWideScaleBytes) return -1.0;
     const WideDevice *wd = wide_device();
-    return wd && wide_config(g, n, wd->cus).groups >= wd->cus;
+    if (!wd || wd->cus <= 0) return -1.0;
+    static constexpr double kUsPerOctet[4] = {1.6, 1.2, 0.85, 0.75};
+    const WideConfig c = wide_config(g, n, wd->cus);
+    const int64_t active = int64_t(c.row_groups) * c.col_groups;
+    const int64_t rounds = ceil_div(active, int64_t(wd->cus));
+    return double(rounds) * double(g.octets) * kUsPerOctet[c.shape] + 2.0;
+}
+
+template <class S>
+static void launch_wide_shape(int fmt, const WideConfig &c, const Geometry &g, const uint8_t *wq, const uint8_t *ws,
+                              float tscale, const uint16_t *X, int n, float *Y, int vec, hipStream_t stream) {
+    if (fmt == kMxfp4)
+        hipLaunchKernelGGL(wide_kernel_mxfp4<S>, dim3(unsigned(c.groups)), dim3(kWideWaves * kLanes), S::kLds,
+                           stream, wq, ws, tscale, int(g.rows), int(g.supertiles), int(g.octets), int(g.cols), X, n,
+                           Y, c.row_groups, c.col_groups, c.extra, vec);
+    else
+        hipLaunchKernelGGL(wide_kernel_nvfp4<S>, dim3(unsigned(c.groups)), dim3(kWideWaves * kLanes), S::kLds,
+                           stream, wq, ws, tscale, int(g.rows), int(g.supertiles), int(g.octets), int(g.cols), X, n,
+                           Y, c.row_groups, c.col_groups, c.extra, vec);
 }
 
 int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float tscale, const uint16_t *X,
@@ -507,14 +592,12 @@ int launch_mfma(const Geometry &g, const uint8_t *wq, const uint8_t *ws, float t
     const WideConfig c = wide_config(g, n, wd->cus);
     if (c.groups > (int64_t(1) << 31) - 1) return NVFP4_ESHAPE;
     const int vec = int(aligned(Y, 16) && g.rows % 4 == 0);
-    if (fmt == kMxfp4)
-        hipLaunchKernelGGL(wide_kernel_mxfp4, dim3(unsigned(c.groups)), dim3(kWideWaves * kLanes), kWideLds,
-                           stream, wq, ws, tscale, int(g.rows), int(g.supertiles), int(g.octets), int(g.cols), X, n,
-                           Y, c.row_groups, c.col_groups, c.extra, vec);
-    else
-        hipLaunchKernelGGL(wide_kernel_nvfp4, dim3(unsigned(c.groups)), dim3(kWideWaves * kLanes), kWideLds,
-                           stream, wq, ws, tscale, int(g.rows), int(g.supertiles), int(g.octets), int(g.cols), X, n,
-                           Y, c.row_groups, c.col_groups, c.extra, vec);
+    switch (c.shape) {
+        case kShapeMid128: launch_wide_shape<ShapeMid128>(fmt, c, g, wq, ws, tscale, X, n, Y, vec, stream); break;
+        case kShapeMid64: launch_wide_shape<ShapeMid64>(fmt, c, g, wq, ws, tscale, X, n, Y, vec, stream); break;
+        case kShapeMid32: launch_wide_shape<ShapeMid32>(fmt, c, g, wq, ws, tscale, X, n, Y, vec, stream); break;
+        default: launch_wide_shape<ShapeProduct>(fmt, c, g, wq, ws, tscale, X, n, Y, vec, stream); break;
+    }
     return launch_status();
 }
 

@@ -131,15 +131,19 @@ int nvfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t ro
  * the batched K+1 verify; qwentin README, "How it works": each weight read
  * once for all columns; wide prefill for large n).
  * Products are exact in fp32 and accumulate in fp32 in a fixed order that
- * depends only on (rows, cols, n): results are bitwise reproducible run to
- * run, and wherever the matvec runs, column c equals, bit for bit, the n = 1
- * product of X[c] (bw24 wiki, exactness note: summation order is part of the
- * contract).  n <= 8 runs the matvec (block dot products on MFMA, block
- * scales and the running sum in fp32 on the VALU; cols <= 2^26, else
- * NVFP4_ESHAPE).  9 <= n <= 16 runs it in two passes (columns 0..7, then the
- * rest), and 17 <= n <= 32 in three or four where the wide contraction's
- * workgroups would not fill the device's CUs; other n (and cols > 2^26) run
- * a dequant-to-bf16 MFMA tile contraction.  1 <= n <= NVFP4_MAX_N.
+ * depends only on (rows, cols, n) and the device's CU count: results are
+ * bitwise reproducible run to run; wherever the matvec runs, column c
+ * equals, bit for bit, the n = 1 product of X[c], and wherever the MFMA
+ * contraction runs, the same column of any wider contraction (bw24 wiki,
+ * exactness note: summation order is part of the contract).  n <= 8 runs
+ * the matvec (block dot products on MFMA, block scales and the running sum
+ * in fp32 on the VALU; cols <= 2^26, else NVFP4_ESHAPE).  9 <= n <= 128
+ * runs either the matvec in passes of up to eight columns (columns 0..7,
+ * then 8..15, ...) or a dequant-to-bf16 MFMA tile contraction, whichever a
+ * cost model of the two on the device's CU count estimates faster (the
+ * contraction takes rows of at most 2^22 elements, the passes 2^26);
+ * n > 128 runs the contraction (cols <= 2^22, else NVFP4_ESHAPE).
+ * 1 <= n <= NVFP4_MAX_N.
  * X [n][cols] bf16 bits, Y [n][rows]. */
 int nvfp4_gemv(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t rows, int64_t cols,
                const uint16_t *X, int n, float *Y, hipStream_t stream);
@@ -295,11 +299,11 @@ int mxfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, int64_t ro
                   float *out_f32, uint16_t *out_bf16, hipStream_t stream);
 
 /* nvfp4_gemv for MXFP4 weights: the same products (n <= 8 the matvec with
- * each 32-element block's dot product on MFMA and its scale in fp32, in
- * passes for 9..32 columns as nvfp4_gemv; other n the dequant-to-bf16 MFMA
- * contraction, decoding with one scaled
- * conversion per two elements), the same fixed summation order and column
- * identity.  Domain: the sums run in fp32 (the wide product's decoded
+ * each 32-element block's dot product on MFMA and its scale in fp32; 9..128
+ * columns in passes of it or the dequant-to-bf16 MFMA contraction by the
+ * same cost model as nvfp4_gemv; past 128 the contraction, decoding with one
+ * scaled conversion per two elements), the same fixed summation order and
+ * column identity.  Domain: the sums run in fp32 (the wide product's decoded
  * weights in bf16, the same exponent range) before the tensor scale, so a
  * weight whose e2m1 * 2^(b - 127) passes fp32's range (scale bytes 253 and
  * 254 with |e2m1| >= 4 resp. >= 2) makes its outputs infinite or NaN even

@@ -187,15 +187,18 @@ def test_gemv_validation(lib):
     assert g(A, B, 1.0, 16, 32, MIS, 1, A, S0) == EALIGN
     assert g(A, B, 1.0, 16, 32, C, 1, ctypes.c_void_p(0x100002), S0) == EALIGN
     assert g(A, B, 1.0, 16, 32, C, 1, NULL, S0) == EINVAL
-    # the matvec (n <= 8, and its passes for 9..32 columns) takes rows of at
-    # most 2^26 elements, the wide product (every larger n) rows of at most
-    # 2^22.  Every call here must fail validation: nothing may launch.
+    # the matvec (n <= 8, and its passes, which 9..128 columns may take) takes
+    # rows of at most 2^26 elements, the wide product rows of at most 2^22;
+    # past 128 columns only the wide product runs.  Every call here must fail
+    # validation: nothing may launch.  (9..128 columns with rows between 2^22
+    # and 2^26 elements are valid: they run as passes.)
     assert g(A, B, 1.0, 16, (1 << 26) + 16, C, 8, A, S0) == ESHAPE
     assert g(A, B, 1.0, 16, (1 << 26) + 16, C, 16, A, S0) == ESHAPE    # passes impossible, wide too wide
-    assert g(A, B, 1.0, 16, (1 << 22) + 32, C, 33, A, S0) == ESHAPE
+    assert g(A, B, 1.0, 16, (1 << 26) + 16, C, 128, A, S0) == ESHAPE
+    assert g(A, B, 1.0, 16, (1 << 22) + 32, C, 129, A, S0) == ESHAPE   # wide only, too wide
     assert lib.mxfp4_gemv(A, B, 1.0, 16, (1 << 26) + 32, C, 8, A, S0) == ESHAPE
     assert lib.mxfp4_gemv(A, B, 1.0, 16, (1 << 26) + 32, C, 16, A, S0) == ESHAPE
-    assert lib.mxfp4_gemv(A, B, 1.0, 16, (1 << 22) + 32, C, 33, A, S0) == ESHAPE
+    assert lib.mxfp4_gemv(A, B, 1.0, 16, (1 << 22) + 32, C, 129, A, S0) == ESHAPE
 
 
 def test_argmax_validation(lib):

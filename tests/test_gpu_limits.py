@@ -1,8 +1,11 @@
 """GPU parity at the largest shapes the products accept: rows of 2^26
-elements for the matvec (n <= 8, and its passes over 9..32 columns; its
-32-bit buffer offsets reach 2^31 bytes per super-tile stream) and of 2^22
-elements for the wide contraction, in both formats; one block past either
-limit is rejected on the host (tests/test_abi_host.py)."""
+elements for the matvec (n <= 8, and its passes, which 9..128 columns may
+take; its 32-bit buffer offsets reach 2^31 bytes per super-tile stream) and
+of 2^22 elements for the wide contraction, in both formats; one block past
+either limit is rejected on the host (tests/test_abi_host.py).  The wide
+case runs 129 columns, which only the wide product takes: the product
+shape's two column tiles, the second at an offset of 2^30 bytes into X;
+the narrower shapes' offsets are bounded by the product shape's."""
 import numpy as np
 import pytest
 import torch
@@ -69,5 +72,5 @@ def test_matvec_passes_at_max_cols(fmt):
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 def test_wide_at_max_cols(fmt):
-    G.note("limits wide %s 16x%d n=33" % (fmt, MAX_WIDE_COLS))
-    _run(fmt, 16, MAX_WIDE_COLS, 33, 201)
+    G.note("limits wide %s 16x%d n=129" % (fmt, MAX_WIDE_COLS))
+    _run(fmt, 16, MAX_WIDE_COLS, 129, 201)

@@ -240,15 +240,17 @@ def test_gemv_deterministic_and_column_identity(R, K):
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
-@pytest.mark.parametrize("R,K", [
-    (17408, 5120),   # the wide product's workgroups leave CUs idle: passes up to 32 columns
-    (1000, 2080),    # ragged rows and octets
+@pytest.mark.parametrize("R,K,widths", [
+    (17408, 5120, (9, 16)),             # two passes beat the wide product; from 17 columns it wins
+    (4096, 4096, (9, 17, 24, 32, 40)),  # the wide product's 32 workgroups: passes to 40 columns
+    (1000, 2080, (9, 12, 16, 32)),      # ragged rows and octets
 ])
-def test_matvec_passes_column_identity(fmt, R, K):
-    """9..32 columns run as passes of the matvec where they are faster than
-    the wide product (always up to 16): column c then has the bits of the
-    one-column product of X[c], and every output is within the parity
-    tolerance of the oracle."""
+def test_matvec_passes_column_identity(fmt, R, K, widths):
+    """9..128 columns run as passes of the matvec where the cost model
+    estimates them faster than the wide product (on 256 CUs: 17408 x 5120 to
+    16 columns, 4096 x 4096 to 40, 1000 x 2080 past 32): column c then has
+    the bits of the one-column product of X[c], and every output is within
+    the parity tolerance of the oracle."""
     mx = fmt == "mxfp4"
     W = G.seeded_matrix(R, K, 31)
     if mx:
@@ -261,11 +263,12 @@ def test_matvec_passes_column_identity(fmt, R, K):
     else:
         wq, ws, c_ref, s_ref = _prepare(R, K, 31)
     f = nv.mxfp4_gemv if mx else nv.nvfp4_gemv
-    X = G.seeded_x(32, K, seed=32)
-    singles = torch.full((32, R), float("nan"), dtype=torch.float32, device=G.DEV)
-    for c in range(32):
+    cols = max(widths)
+    X = G.seeded_x(cols, K, seed=32)
+    singles = torch.full((cols, R), float("nan"), dtype=torch.float32, device=G.DEV)
+    for c in range(cols):
         f(wq, ws, 0.5, R, K, X[c:c + 1].contiguous(), 1, singles[c:c + 1])
-    for n in (9, 12, 16) if R < 10000 else (9, 16, 17, 24, 32):
+    for n in widths:
         G.note("passes %s %dx%d n=%d" % (fmt, R, K, n))
         y = torch.full((n, R), float("nan"), dtype=torch.float32, device=G.DEV)
         f(wq, ws, 0.5, R, K, X[:n].contiguous(), n, y)
