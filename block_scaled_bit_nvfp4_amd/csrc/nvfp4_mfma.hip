@@ -13,9 +13,10 @@
 // one E8M0 byte per 32 elements and decodes e2m1 * 2^(b - 127) in the scaled
 // conversion itself (exact for every finite byte).
 //
-// Tiling.  Two waves per SIMD, so that one wave's weight decode (VALU) runs
-// while the other's MFMAs execute.  A workgroup of eight waves owns four
-// 64-row super-tiles x 128 activation columns; wave w takes two tiles
+// Tiling (the product shape; WideShape below gives the narrower shapes that
+// serve 9..128 columns).  Two waves per SIMD, so that one wave's weight
+// decode (VALU) runs while the other's MFMAs execute.  A workgroup of eight
+// waves owns four 64-row super-tiles x 128 activation columns; wave w takes two tiles
 // (32 rows) of super-tile w / 2 over all 128 columns (64 fp32 accumulators
 // per lane, in AGPRs).  The workgroup's X tile (128 columns) is staged in
 // LDS one octet (128 k) at a time through a ring of two buffers by
