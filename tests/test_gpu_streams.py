@@ -80,3 +80,35 @@ def test_two_streams_equal_sequential():
         for got, want in ((_results(o0), ref0), (_results(o1), ref1)):
             for g_, w_ in zip(got, want):
                 assert torch.equal(g_.view(torch.int32), w_.view(torch.int32)), rep
+
+
+def test_two_streams_split_finish():
+    """Two argmax calls whose finish runs split (270000 and 200000 rows of 16
+    columns at two columns: 16876 and 12500 keys), on two streams at once,
+    each counting on the counter in its own workspace: the rows of the
+    sequential calls."""
+    K, n = 16, 2
+    a, b = _mat(270000, K, 65), _mat(200000, K, 66)
+    X0, X1 = G.seeded_x(n, K, seed=67), G.seeded_x(n, K, seed=68)
+    am0, am1 = (torch.full((n,), -7, dtype=torch.int32, device=G.DEV) for _ in range(2))
+    w0 = torch.full((nv.nvfp4_gemv_argmax_workspace_bytes(270000, K, n),), 0xA5, dtype=torch.uint8, device=G.DEV)
+    w1 = torch.full((nv.nvfp4_gemv_argmax_workspace_bytes(200000, K, n),), 0xA5, dtype=torch.uint8, device=G.DEV)
+    G.note("streams split finish: sequential")
+    nv.nvfp4_gemv_argmax(a[0], a[1], 1.0, 270000, K, X0, n, None, am0, w0)
+    nv.nvfp4_gemv_argmax(b[0], b[1], 1.0, 200000, K, X1, n, None, am1, w1)
+    torch.cuda.synchronize()
+    ref0, ref1 = am0.clone(), am1.clone()
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        am0.fill_(-7)
+        am1.fill_(-7)
+        torch.cuda.synchronize()
+        G.note("streams split finish: concurrent %d" % rep)
+        for _ in range(4):
+            with torch.cuda.stream(s0):
+                nv.nvfp4_gemv_argmax(a[0], a[1], 1.0, 270000, K, X0, n, None, am0, w0)
+            with torch.cuda.stream(s1):
+                nv.nvfp4_gemv_argmax(b[0], b[1], 1.0, 200000, K, X1, n, None, am1, w1)
+        torch.cuda.synchronize()
+        assert torch.equal(am0, ref0), rep
+        assert torch.equal(am1, ref1), rep
