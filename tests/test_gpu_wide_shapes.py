@@ -122,3 +122,45 @@ def test_small_matrix_keeps_passes():
     for c in (0, 7, 8, 15, 16, 23):
         y1 = G.gemv_gpu(wq, ws, 1.0, r, k, X[c:c + 1].contiguous())
         assert torch.equal(Y[c].view(torch.int32), y1[0].view(torch.int32)), c
+
+
+@pytest.mark.parametrize("fmt,k", [("nvfp4", 5136), ("mxfp4", 5152)])
+def test_shapes_ragged(fmt, k):
+    """17401 rows (a partial last super-tile; rows not a multiple of four,
+    so the outputs go out one by one) and a partial last octet: 20, 33, 47
+    and 97 columns (32-, 64-, 64- and 128-column shapes) equal the same
+    columns of a 200-column product bit for bit, which matches the oracle on
+    sampled rows, the last ones included."""
+    r = 17401
+    W = G.seeded_matrix(r, k, 405)
+    codes = torch.empty(r, k // 2, dtype=torch.uint8, device=G.DEV)
+    if fmt == "mxfp4":
+        scales = torch.empty(r, k // 32, dtype=torch.uint8, device=G.DEV)
+        nv.mxfp4_quantize(W, r, k, 1.0, codes, scales)
+        wq, ws = nv.alloc_mx_repacked(r, k, G.DEV)
+        nv.mxfp4_repack(codes, scales, r, k, wq, ws)
+    else:
+        scales = torch.empty(r, k // 16, dtype=torch.uint8, device=G.DEV)
+        nv.nvfp4_quantize(W, r, k, 1.0, codes, scales)
+        wq, ws = nv.alloc_repacked(r, k, G.DEV)
+        nv.nvfp4_repack(codes, scales, r, k, wq, ws)
+    f = _gemv(fmt)
+    X = G.seeded_x(200, k, seed=406)
+    Y = torch.full((200, r), float("nan"), dtype=torch.float32, device=G.DEV)
+    G.note("wide shapes ragged %s %dx%d n=200" % (fmt, r, k))
+    f(wq, ws, 1.5, r, k, X, 200, Y)
+    for n in (20, 33, 47, 97):
+        G.note("wide shapes ragged %s %dx%d n=%d" % (fmt, r, k, n))
+        y = torch.full((n, r), float("nan"), dtype=torch.float32, device=G.DEV)
+        f(wq, ws, 1.5, r, k, X[:n].contiguous(), n, y)
+        assert torch.equal(y.view(torch.int32), Y[:n].view(torch.int32)), (fmt, n)
+    rows = np.array([0, 5, 63, 64, 9999, 17343, 17344, 17399, 17400])
+    Wc = W[torch.as_tensor(rows, device=G.DEV)].cpu().numpy()
+    if fmt == "mxfp4":
+        c_ref, s_ref = oracle.mx_quantize(Wc, 1.0)
+        Y_ref, S = oracle.mx_gemv(c_ref, s_ref, 1.5, G.wl.bf16_bits(X))
+    else:
+        c_ref, s_ref = oracle.quantize(Wc, 1.0)
+        Y_ref, S = oracle.gemv(c_ref, s_ref, 1.5, G.wl.bf16_bits(X))
+    G.assert_within_tolerance(Y[:, torch.as_tensor(rows, device=G.DEV)].cpu().numpy(), Y_ref, S,
+                              "wide shapes ragged %s sampled rows" % fmt)
