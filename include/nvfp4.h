@@ -49,7 +49,9 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are device memory owned by the caller; the library
- *     allocates nothing and keeps no state between calls.  Inputs must not be
+ *     allocates nothing, and the only state it keeps between calls are facts
+ *     it looks up once per device (the CU count, the wide kernels' LDS limit,
+ *     the address of nvfp4_gemv_argmax_noalloc's array).  Inputs must not be
  *     modified, and outputs not read, until the call's work on `stream` is
  *     done.  `stream` may be NULL (the null stream).
  *   - Calls are asynchronous and stream-ordered: arguments are validated on
