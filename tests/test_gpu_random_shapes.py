@@ -8,7 +8,13 @@ The argmax must equal the argmax of the GPU's own logits (lowest index on
 ties) and the oracle's, except where the oracle's two leading values lie
 within the parity tolerance of each other: there either index is a correct
 answer at fp32 (the configured workloads are checked for identity
-elsewhere)."""
+elsewhere).
+
+A second sweep takes wide n (9 to 600: the passes of the matvec and every
+workgroup shape of the MFMA contraction, as the cost model picks them) on
+ragged rows and rows of any whole number of blocks, checks every column on
+sampled rows against the oracle, and requires a second call to repeat the
+bits."""
 import numpy as np
 import pytest
 import torch
@@ -117,3 +123,59 @@ def test_random_shape(R, K, n, tscale, mx, seed):
     assert torch.equal(a1, am), what + ": batched argmax"
     assert torch.equal(y2.view(torch.int32), G.gemv_gpu(wq2, ws2, 1.0, R2, K, X).view(torch.int32)), \
         what + ": batched second product"
+
+
+def _wide_cases(count=44, seed=777):
+    """Rows log-uniform over 20..60000, columns over 2..12000 blocks, n from
+    one of four ranges (9..32, 33..64, 65..128, 129..600), both formats."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        mx = i % 3 == 2
+        step = 32 if mx else 16
+        R = int(np.exp(rng.uniform(np.log(20), np.log(60000))))
+        K = step * max(1, int(np.exp(rng.uniform(np.log(2), np.log(12000 / step)))))
+        n = int(rng.choice([int(rng.integers(9, 33)), int(rng.integers(33, 65)), int(rng.integers(65, 129)),
+                            int(rng.integers(129, 601))]))
+        while R * K > 40_000_000:
+            R = max(1, R // 2)
+        out.append((R, K, n, TSCALES[i % 4], mx, 5000 + i))
+    return out
+
+
+WIDE_CASES = _wide_cases()
+
+
+@pytest.mark.parametrize("R,K,n,tscale,mx,seed", WIDE_CASES,
+                         ids=["%s-%dx%d-n%d" % ("mx" if c[4] else "nv", c[0], c[1], c[2]) for c in WIDE_CASES])
+def test_random_wide_shape(R, K, n, tscale, mx, seed):
+    what = "%s %dx%d n=%d tscale=%g" % ("mxfp4" if mx else "nvfp4", R, K, n, tscale)
+    G.note("random wide " + what)
+    W = G.seeded_matrix(R, K, seed)
+    codes = torch.empty(R, K // 2, dtype=torch.uint8, device=G.DEV)
+    if mx:
+        scales = torch.empty(R, K // 32, dtype=torch.uint8, device=G.DEV)
+        nv.mxfp4_quantize(W, R, K, tscale, codes, scales)
+        wq, ws = nv.alloc_mx_repacked(R, K, G.DEV)
+        nv.mxfp4_repack(codes, scales, R, K, wq, ws)
+    else:
+        codes, scales = G.quantize_gpu(W, tscale)
+        wq, ws = G.repack_gpu(codes, scales, R, K)
+    f = nv.mxfp4_gemv if mx else nv.nvfp4_gemv
+    X = G.seeded_x(n, K, seed=seed + 1)
+    Y = torch.full((n, R), float("nan"), dtype=torch.float32, device=G.DEV)
+    f(wq, ws, tscale, R, K, X, n, Y)
+    Y2 = torch.full((n, R), float("nan"), dtype=torch.float32, device=G.DEV)
+    f(wq, ws, tscale, R, K, X, n, Y2)
+    assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32)), what + ": a second call differs"
+    rng = np.random.default_rng(seed)
+    rows = np.array(sorted(set([0, R // 2, R - 1] + [int(r) for r in rng.integers(0, R, size=min(R, 24))])))
+    sel = torch.as_tensor(rows, device=G.DEV)
+    Wc = W[sel].cpu().numpy()
+    if mx:
+        c_ref, s_ref = oracle.mx_quantize(Wc, tscale)
+        Y_ref, S = oracle.mx_gemv(c_ref, s_ref, tscale, G.wl.bf16_bits(X))
+    else:
+        c_ref, s_ref = oracle.quantize(Wc, tscale)
+        Y_ref, S = oracle.gemv(c_ref, s_ref, tscale, G.wl.bf16_bits(X))
+    G.assert_within_tolerance(Y[:, sel].cpu().numpy(), Y_ref, S, what + " (sampled rows)")
