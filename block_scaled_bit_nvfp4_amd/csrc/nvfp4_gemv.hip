@@ -330,14 +330,18 @@ argmax_finish_kernel(const unsigned long long *__restrict__ keys, int groups, in
 
 // The split finish: workgroup w reduces its share of the groups to N
 // partial maxima, stores them to the header and counts itself on the
-// header's counter with an agent-scope release add (the barrier before it
-// orders the other threads' part stores before the add); the workgroup that
+// header's counter with an agent-scope release add; the workgroup that
 // counts last takes an agent-scope acquire fence, reads the kFinishGroups x N
-// parts and writes the indices.  On gfx950 the release is an L2 write-back
+// parts and writes the indices.  The part stores come from threads 0 .. N - 1
+// (N <= 8), all in the first wave, whose thread 0 also makes the release add:
+// the release covers them as that wave's own earlier stores (the L2
+// write-back and the wait for the wave's outstanding stores come before the
+// add), whatever the workgroup barrier between them does or does not wait for.  On gfx950 the release is an L2 write-back
 // and the acquire an L2 invalidate (the XCDs' L2s are not coherent); with
 // the L2 holding only the parts, both measured within noise of leaving them
 // out.  The product zeroed the counter.
 constexpr int kSplitFinishThreads = 256;
+static_assert(kMaxNarrowN <= kLanes, "the split finish's part stores come from its first wave");
 
 template <int N>
 __global__ void __launch_bounds__(kSplitFinishThreads)
