@@ -502,9 +502,10 @@ int launch_gemv_swiglu(const uint8_t *wq, const uint8_t *ws, float tscale, int64
     const Geometry g(2 * F, hidden);
     if (!swiglu_fusable(g, F, n)) {
         // The plain product into gu, then the SwiGLU kernel: the same bits.
-        if (!gu) return NVFP4_ESHAPE;
+        const unsigned grid = grid_1d(F * n, 256);
+        if (!gu || !grid) return NVFP4_ESHAPE;
         if (int st = launch_narrow<kPlain>(g, wq, ws, tscale, X, n, gu, nullptr, stream)) return st;
-        hipLaunchKernelGGL(swiglu_kernel, dim3(unsigned(ceil_div(F * n, 256))), dim3(256), 0, stream, gu, F,
+        hipLaunchKernelGGL(swiglu_kernel, dim3(grid), dim3(256), 0, stream, gu, F,
                            F * n, h);
         return launch_status();
     }
@@ -684,8 +685,10 @@ NVFP4_API int nvfp4_swiglu(const float *gu, int64_t F, int n, uint16_t *h, hipSt
     if (F < 1 || F > (int64_t(1) << 40)) return NVFP4_ESHAPE;
     if (!aligned(gu, 16) || !aligned(h, 4)) return NVFP4_EALIGN;
     const int64_t total = F * n;
+    const unsigned grid = grid_1d(total, 256);
+    if (!grid) return NVFP4_ESHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(swiglu_kernel, dim3(unsigned(ceil_div(total, 256))), dim3(256), 0, stream, gu, F, total, h);
+    hipLaunchKernelGGL(swiglu_kernel, dim3(grid), dim3(256), 0, stream, gu, F, total, h);
     return launch_status();
 }
 

@@ -46,6 +46,15 @@ struct Geometry {
     size_t scale_bytes(int fmt) const { return fmt == kMxfp4 ? mx_scale_bytes() : scale_bytes(); }
 };
 
+// Workgroups of a one-dimensional launch over `units` items at `threads`
+// per workgroup, or 0 when they would pass the largest grid (2^31 - 1
+// workgroups); the entry points return NVFP4_ESHAPE for 0 before launching,
+// so no grid is ever truncated.
+inline unsigned grid_1d(int64_t units, int threads) {
+    const int64_t g = ceil_div(units, threads);
+    return g < 1 || g > int64_t(0x7FFFFFFF) ? 0u : unsigned(g);
+}
+
 inline int launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP;

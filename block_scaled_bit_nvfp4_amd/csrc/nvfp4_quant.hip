@@ -302,8 +302,10 @@ NVFP4_API int nvfp4_quantize(const float *W, int64_t rows, int64_t cols, float t
     if (int st = check_shape(rows, cols)) return st;
     if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 16)) return NVFP4_EALIGN;
     const int64_t nblocks = rows * (cols / kBlock);
+    const unsigned grid = grid_1d(nblocks, 256);
+    if (!grid) return NVFP4_ESHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(ceil_div(nblocks, 256))), dim3(256), 0, stream,
+    hipLaunchKernelGGL(quantize_kernel, dim3(grid), dim3(256), 0, stream,
                        reinterpret_cast<const float4 *>(W), nblocks, tscale,
                        reinterpret_cast<uint2 *>(codes), scales);
     return launch_status();
@@ -317,8 +319,10 @@ NVFP4_API int nvfp4_repack(const uint8_t *codes, const uint8_t *scales, int64_t 
         return NVFP4_EALIGN;
     const Geometry g(rows, cols);
     const int64_t code_units = int64_t(g.code_bytes() / 16), scale_units = int64_t(g.scale_bytes() / 8);
+    const unsigned grid = grid_1d(code_units + scale_units, 256);
+    if (!grid) return NVFP4_ESHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(repack_kernel<kNvfp4>, dim3(unsigned(ceil_div(code_units + scale_units, 256))), dim3(256),
+    hipLaunchKernelGGL(repack_kernel<kNvfp4>, dim3(grid), dim3(256),
                        0, stream, codes, scales, rows, cols, g.octets, code_units, scale_units,
                        reinterpret_cast<uint4 *>(wq), static_cast<void *>(ws));
     return launch_status();
@@ -332,8 +336,10 @@ NVFP4_API int nvfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, 
         return NVFP4_EALIGN;
     const Geometry g(rows, cols);
     const int64_t code_units = int64_t(g.code_bytes() / 16);
+    const unsigned grid = grid_1d(code_units, 256);
+    if (!grid) return NVFP4_ESHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(dequant_kernel, dim3(unsigned(ceil_div(code_units, 256))), dim3(256), 0, stream,
+    hipLaunchKernelGGL(dequant_kernel, dim3(grid), dim3(256), 0, stream,
                        reinterpret_cast<const uint4 *>(wq), reinterpret_cast<const uint2 *>(ws), tscale,
                        rows, cols, g.octets, code_units, out_f32, out_bf16);
     return launch_status();
@@ -355,8 +361,10 @@ NVFP4_API int mxfp4_quantize(const float *W, int64_t rows, int64_t cols, float t
     if (int st = check_mx_shape(rows, cols)) return st;
     if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(scales, 16)) return NVFP4_EALIGN;
     const int64_t nblocks = rows * (cols / kMxBlock);
+    const unsigned grid = grid_1d(nblocks, 256);
+    if (!grid) return NVFP4_ESHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(mx_quantize_kernel, dim3(unsigned(ceil_div(nblocks, 256))), dim3(256), 0, stream,
+    hipLaunchKernelGGL(mx_quantize_kernel, dim3(grid), dim3(256), 0, stream,
                        reinterpret_cast<const float4 *>(W), nblocks, tscale, reinterpret_cast<uint4 *>(codes),
                        scales);
     return launch_status();
@@ -370,8 +378,10 @@ NVFP4_API int mxfp4_repack(const uint8_t *codes, const uint8_t *scales, int64_t 
         return NVFP4_EALIGN;
     const Geometry g(rows, cols);
     const int64_t code_units = int64_t(g.code_bytes() / 16), scale_units = int64_t(g.mx_scale_bytes() / 4);
+    const unsigned grid = grid_1d(code_units + scale_units, 256);
+    if (!grid) return NVFP4_ESHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(repack_kernel<kMxfp4>, dim3(unsigned(ceil_div(code_units + scale_units, 256))), dim3(256),
+    hipLaunchKernelGGL(repack_kernel<kMxfp4>, dim3(grid), dim3(256),
                        0, stream, codes, scales, rows, cols, g.octets, code_units, scale_units,
                        reinterpret_cast<uint4 *>(wq), static_cast<void *>(ws));
     return launch_status();
@@ -385,8 +395,10 @@ NVFP4_API int mxfp4_dequant(const uint8_t *wq, const uint8_t *ws, float tscale, 
         return NVFP4_EALIGN;
     const Geometry g(rows, cols);
     const int64_t code_units = int64_t(g.code_bytes() / 16);
+    const unsigned grid = grid_1d(code_units, 256);
+    if (!grid) return NVFP4_ESHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(mx_dequant_kernel, dim3(unsigned(ceil_div(code_units, 256))), dim3(256), 0, stream,
+    hipLaunchKernelGGL(mx_dequant_kernel, dim3(grid), dim3(256), 0, stream,
                        reinterpret_cast<const uint4 *>(wq), reinterpret_cast<const uint32_t *>(ws), tscale, rows,
                        cols, g.octets, code_units, out_f32, out_bf16);
     return launch_status();

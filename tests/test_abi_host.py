@@ -225,6 +225,24 @@ def test_other_entry_points_validation(lib):
     assert lib.nvfp4_swiglu(MIS, 16, 1, B, S0) == EALIGN
 
 
+def test_one_dimensional_grids_past_the_largest_are_rejected(lib):
+    """Shapes the layout admits but whose one-workgroup-per-256-items launch
+    would pass 2^31 - 1 workgroups get NVFP4_ESHAPE instead of a truncated
+    grid (every call here is far past the limit, so nothing launches)."""
+    R, K = (1 << 31) - 64, (1 << 31) - 1024          # the largest admitted rows and columns
+    assert lib.nvfp4_repacked_code_bytes(R, K) > 0    # a valid layout...
+    for f in (lib.nvfp4_quantize, lib.mxfp4_quantize):
+        assert f(A, R, K, 1.0, B, C, S0) == ESHAPE
+    # just past the limit: 2^39 + 2^20 blocks of 16 (NVFP4), 2^39 + 2^21 of 32 (MXFP4)
+    assert lib.nvfp4_quantize(A, 1 << 20, (1 << 23) + 32, 1.0, B, C, S0) == ESHAPE
+    assert lib.mxfp4_quantize(A, 1 << 21, (1 << 23) + 32, 1.0, B, C, S0) == ESHAPE
+    for f in (lib.nvfp4_repack, lib.mxfp4_repack):
+        assert f(A, B, R, K, C, A, S0) == ESHAPE
+    for f in (lib.nvfp4_dequant, lib.mxfp4_dequant):
+        assert f(A, B, 1.0, R, K, C, NULL, S0) == ESHAPE
+    assert lib.nvfp4_swiglu(A, 1 << 40, 65536, B, S0) == ESHAPE
+
+
 def test_gemv_swiglu_validation(lib):
     f = lib.nvfp4_gemv_swiglu
     assert f(A, B, 1.0, 512, 1024, C, 1, NULL, NULL, S0) == EINVAL      # h
